@@ -1,0 +1,205 @@
+/*
+ * misa_indexer.h -- C ABI of the MI355X (gfx950) token-level sparse-attention
+ * indexer: the dense DSA indexer, its MISA form (block-pooled head router,
+ * routed-head token scoring, top-k) and the MISA-dagger rerank.
+ *
+ * What the calls compute follows "MISA: Mixture of Indexer Sparse Attention
+ * for Long-Context LLM Inference" (gist.science explainer), Technical Summary
+ * -- Problem Statement (the DSA indexer scores every prefix token with all
+ * H_I heads and keeps a per-query top-k), Methodology: MISA (router over
+ * M = ceil(L/B) mean-pooled blocks keeps h heads; only those heads score the
+ * prefix; top-k of the reduced score), Hierarchical Variant (MISA-dagger: the
+ * routed pass keeps k' candidates, the all-head indexer rescores them and
+ * keeps k) -- and the MISA abstract (heads share one selected token set; a
+ * query-dependent subset of heads).
+ *
+ * Where the pages are silent this library takes these readings:
+ *   - the prefix of a query at position p is tokens 0..p (inclusive);
+ *   - the indexer score of token i is I(i) = sum_j w_j * max(0, q_j . k_i)
+ *     over the scoring heads j (no extra scale: fold it into w);
+ *   - blocks start at token 0; a block's pooled key is the mean of the keys
+ *     present in it; the query's own last block is the mean of its prefix
+ *     tokens in that block;
+ *   - router importance g_j = w'_j * sum_b max(0, q_j . Kbar_b) over the
+ *     query's blocks, w' = w (mode 0) or |w| (mode 1); the top-h heads by
+ *     (g desc, head id asc) are routed;
+ *   - token ranking is (score desc, token id asc); -0.0 ranks as +0.0.
+ *
+ * Conventions for every call
+ *   - Tensor pointers are DEVICE pointers (hipMalloc'd or from a framework
+ *     allocator).  The caller owns every buffer; the library keeps no pointer
+ *     after returning, allocates nothing and holds no global state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues kernels on it: no host synchronisation, no
+ *     allocation, no memset node (graph capture is safe).
+ *   - Workspaces are caller-provided device buffers of at least the size
+ *     misa_workspace_bytes() reports for the same arguments; their contents
+ *     on entry do not matter and are overwritten.  Calls that share a
+ *     workspace must be ordered on one stream.
+ *   - Selected-token outputs idx[T][k] are SETS: the order of the k entries of
+ *     a row is unspecified.  A slot with no token holds idx = -1 and
+ *     score = -inf (a prefix, or a candidate list, shorter than k).
+ *   - Only host-visible arguments are validated, all before any HIP call; a
+ *     failed check returns a negative status and enqueues nothing.  Values
+ *     that live on the device (q_pos < seq_lens[q_seq], head and candidate
+ *     ids in range and distinct) are NOT checked: out-of-range values are
+ *     undefined behaviour.  A launch error returns MISA_ERR_HIP.  No C++
+ *     exception crosses the boundary.
+ */
+#ifndef MISA_INDEXER_H
+#define MISA_INDEXER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MISA_OK 0
+#define MISA_ERR_NULL (-1)        /* a required pointer is NULL                 */
+#define MISA_ERR_SHAPE (-2)       /* a size or count is out of range            */
+#define MISA_ERR_UNSUPPORTED (-3) /* a valid request this build does not handle */
+#define MISA_ERR_WORKSPACE (-4)   /* workspace smaller than required            */
+#define MISA_ERR_HIP (-5)         /* a HIP launch or runtime call failed        */
+
+/* The key dimension this build supports. */
+#define MISA_D 128
+/* Largest number of indexer heads H (and routed heads h). */
+#define MISA_MAX_HEADS 128
+
+/*
+ * One batch of indexer inputs.  All pointers are device pointers.
+ *   keys     bf16 bits [S][Lmax][d], row-major: one indexing key per token,
+ *            shared by all heads (MISA abstract).
+ *   seq_lens int32 [S]: keys present in each sequence (read by misa_pool).
+ *   q        bf16 bits [T][H][d]: H indexer-head queries per query row.
+ *   w        fp32 [T][H]: per-query head weights.
+ *   q_seq    int32 [T]: the sequence of each query row.
+ *   q_pos    int32 [T]: the position p_t of each query; its prefix is 0..p_t.
+ * d must equal MISA_D; 1 <= H <= MISA_MAX_HEADS; S, T, Lmax >= 1.
+ */
+typedef struct misa_batch {
+  const uint16_t *keys;
+  const int32_t *seq_lens;
+  const uint16_t *q;
+  const float *w;
+  const int32_t *q_seq;
+  const int32_t *q_pos;
+  int32_t S, Lmax, d, T, H;
+} misa_batch;
+
+/* Operation selector for misa_workspace_bytes. */
+#define MISA_OP_DENSE 0       /* indexer_dense                        */
+#define MISA_OP_ROUTE 1       /* misa_route                           */
+#define MISA_OP_SCORE_TOPK 2  /* misa_score_topk                      */
+#define MISA_OP_RERANK 3      /* misa_rerank                          */
+#define MISA_OP_TOPK 4        /* misa_topk (b->T rows of b->Lmax)     */
+
+/*
+ * misa_workspace_bytes: device workspace needed by operation `op` for this
+ * batch shape.  B is the block size (MISA_OP_ROUTE), h the routed head count
+ * (MISA_OP_ROUTE / MISA_OP_SCORE_TOPK), k the selection size, kc the
+ * candidate count (MISA_OP_RERANK).  Only the shape fields of `b` are read.
+ * Writes the size to *bytes; returns a status.
+ */
+int misa_workspace_bytes(const misa_batch *b, int32_t op, int32_t B, int32_t h,
+                         int32_t k, int32_t kc, size_t *bytes);
+
+/*
+ * misa_pool -- mean-pooled indexing keys (Methodology: MISA, Lightweight
+ * Block-Pooled Router: the prefix is cut into M = ceil(L/B) blocks
+ * summarised by mean-pooled indexing keys).
+ *   pooled  fp32 [S][ceil(Lmax/B)][d] (output): pooled[s][b] = mean of
+ *           keys[s][i] over i in [bB, min(bB+B, seq_lens[s])); a block with
+ *           no key present is written as zeros.
+ * Run once per key cache (and again after keys are appended); misa_route
+ * reads it.  Uses keys, seq_lens, S, Lmax, d.  1 <= B <= Lmax.
+ */
+int misa_pool(const misa_batch *b, int32_t B, float *pooled, void *stream);
+
+/*
+ * misa_route -- the block-pooled head router (Methodology: MISA,
+ * Lightweight Block-Pooled Router; the MISA abstract's query-dependent
+ * subset of heads).  For query t with b_t = floor(p_t / B):
+ *   g[t][j] = w'_j * ( sum_{b < b_t} max(0, q_j . pooled[s][b])
+ *                      + max(0, q_j . mean(keys[s][b_t*B .. p_t])) ),
+ * w' = w (mode 0) or |w| (mode 1); heads[t][0..h) = the top-h heads by
+ * (g desc, head id asc), in that rank order.
+ *   pooled      misa_pool's output for the same keys and the same B; only
+ *               complete blocks b < b_t are read, the query's own last block
+ *               is pooled from the keys.
+ *   heads       int32 [T][h] (output).
+ *   head_score  fp32 [T][H] (output, may be NULL): g.
+ *   ws/ws_bytes workspace (MISA_OP_ROUTE).
+ * 1 <= h <= H; mode in {0, 1}; 1 <= B <= Lmax.
+ */
+int misa_route(const misa_batch *b, const float *pooled, int32_t B, int32_t h,
+               int32_t mode, int32_t *heads, float *head_score, void *ws,
+               size_t ws_bytes, void *stream);
+
+/*
+ * misa_score -- indexer score rows (Methodology: MISA, Sparse Token Scoring;
+ * with heads == NULL, the dense DSA indexer of the Problem Statement).
+ *   heads   int32 [T][h] routed head ids, or NULL for all H heads.
+ *   scores  fp32 [T][Lmax] (output): I(i) for i <= p_t, -inf for i > p_t.
+ * bf16 products, fp32 accumulation.  1 <= h <= H when heads != NULL.
+ */
+int misa_score(const misa_batch *b, const int32_t *heads, int32_t h,
+               float *scores, void *stream);
+
+/*
+ * misa_topk -- per-row top-k of fp32 score rows by (score desc, index asc).
+ *   scores   fp32 [rows][ld]; row r's candidates are columns [0, row_len[r]).
+ *   row_len  int32 [rows] (device), each in [0, ld].
+ *   idx      int32 [rows][k] (output), val fp32 [rows][k] (output, may be
+ *            NULL): the selected columns and their scores (a set).
+ * Scores must not be NaN.  ws: MISA_OP_TOPK with the batch {T=rows, Lmax=ld}.
+ */
+int misa_topk(const float *scores, int32_t rows, int32_t ld,
+              const int32_t *row_len, int32_t k, int32_t *idx, float *val,
+              void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * misa_score_topk -- routed token scoring and per-query top-k (Methodology:
+ * MISA, Sparse Token Scoring).  With k = k' this is MISA-dagger's Coarse
+ * Stage (Hierarchical Variant).
+ *   heads   int32 [T][h] (misa_route's output), or NULL for all H heads.
+ *   idx     int32 [T][k] (output) selected token ids, val fp32 [T][k]
+ *           (output, may be NULL) their scores.
+ * 1 <= k <= Lmax.  ws: MISA_OP_SCORE_TOPK.
+ */
+int misa_score_topk(const misa_batch *b, const int32_t *heads, int32_t h,
+                    int32_t k, int32_t *idx, float *val, void *ws,
+                    size_t ws_bytes, void *stream);
+
+/*
+ * indexer_dense -- the DSA lightning indexer: all H heads score every
+ * prefix key, then the per-query top-k (Problem Statement).  Same outputs as
+ * misa_score_topk with heads == NULL.  ws: MISA_OP_DENSE.
+ */
+int indexer_dense(const misa_batch *b, int32_t k, int32_t *idx, float *val,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * misa_rerank -- MISA-dagger's Fine Stage (Hierarchical Variant): the
+ * all-head indexer rescores only the candidates and keeps the top-k.
+ *   cand    int32 [T][kc]: distinct token ids of query t's prefix, -1 for an
+ *           empty slot (misa_score_topk's idx with k = kc).
+ *   idx     int32 [T][k] (output) token ids, val fp32 [T][k] (output, may be
+ *           NULL) their all-head scores, ranked (score desc, token id asc).
+ * 1 <= k <= kc.  ws: MISA_OP_RERANK.
+ */
+int misa_rerank(const misa_batch *b, const int32_t *cand, int32_t kc, int32_t k,
+                int32_t *idx, float *val, void *ws, size_t ws_bytes,
+                void *stream);
+
+/* misa_status_str -- a static English description of a status code. */
+const char *misa_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MISA_INDEXER_H */

@@ -1,0 +1,244 @@
+"""Thin Python binding of ``libmisa_indexer.so`` (C ABI in include/misa_indexer.h).
+
+Argument marshalling only: torch tensors supply device memory and the
+current HIP stream; every step of the indexer runs in the library's gfx950
+kernels.  There is no fallback: if the library is missing or no GPU is
+visible, the calls raise.
+
+Tensor formats (all on the GPU, contiguous):
+  keys  bf16 [S][Lmax][128]   q bf16 [T][H][128]   w fp32 [T][H]
+  seq_lens, q_seq, q_pos int32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmisa_indexer.so")
+
+MISA_OP_DENSE, MISA_OP_ROUTE, MISA_OP_SCORE_TOPK, MISA_OP_RERANK, MISA_OP_TOPK = range(5)
+
+# Every entry point include/misa_indexer.h declares.
+EXPORTS = ("misa_workspace_bytes", "misa_pool", "misa_route", "misa_score", "misa_topk",
+           "misa_score_topk", "indexer_dense", "misa_rerank", "misa_status_str")
+
+
+class MisaBatch(ctypes.Structure):
+    _fields_ = [("keys", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("q", ctypes.c_void_p), ("w", ctypes.c_void_p),
+                ("q_seq", ctypes.c_void_p), ("q_pos", ctypes.c_void_p),
+                ("S", ctypes.c_int32), ("Lmax", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("T", ctypes.c_int32), ("H", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SZ = ctypes.c_size_t
+_lib = None
+
+
+def load():
+    """Load the library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libmisa_indexer.so is not built; run "
+                              "`python -m long_context_sparse_05_amd.build_lib`")
+        L = ctypes.CDLL(LIB_PATH)
+        BP = ctypes.POINTER(MisaBatch)
+        L.misa_workspace_bytes.argtypes = [BP, _I, _I, _I, _I, _I, ctypes.POINTER(_SZ)]
+        L.misa_pool.argtypes = [BP, _I, _P, _P]
+        L.misa_route.argtypes = [BP, _P, _I, _I, _I, _P, _P, _P, _SZ, _P]
+        L.misa_score.argtypes = [BP, _P, _I, _P, _P]
+        L.misa_topk.argtypes = [_P, _I, _I, _P, _I, _P, _P, _P, _SZ, _P]
+        L.misa_score_topk.argtypes = [BP, _P, _I, _I, _P, _P, _P, _SZ, _P]
+        L.indexer_dense.argtypes = [BP, _I, _P, _P, _P, _SZ, _P]
+        L.misa_rerank.argtypes = [BP, _P, _I, _I, _P, _P, _P, _SZ, _P]
+        for name in EXPORTS:
+            getattr(L, name).restype = ctypes.c_int
+        L.misa_status_str.argtypes = [ctypes.c_int]
+        L.misa_status_str.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_str(code: int) -> str:
+    return load().misa_status_str(int(code)).decode()
+
+
+def _check(code, what):
+    if code != 0:
+        raise RuntimeError("%s: %s (status %d)" % (what, status_str(code), code))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, name, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims" % (name, ndim))
+    return t
+
+
+class Batch:
+    """Device-resident indexer inputs plus the ABI struct describing them."""
+
+    def __init__(self, keys, q, w, q_seq, q_pos, seq_lens=None):
+        torch = _torch()
+        self.keys = _need(keys, torch.bfloat16, "keys", 3)
+        self.q = _need(q, torch.bfloat16, "q", 3)
+        self.w = _need(w, torch.float32, "w", 2)
+        self.q_seq = _need(q_seq, torch.int32, "q_seq", 1)
+        self.q_pos = _need(q_pos, torch.int32, "q_pos", 1)
+        S, Lmax, d = self.keys.shape
+        T, H, dq = self.q.shape
+        if dq != d or tuple(self.w.shape) != (T, H) or self.q_seq.numel() != T or self.q_pos.numel() != T:
+            raise ValueError("inconsistent batch shapes")
+        if seq_lens is None:
+            seq_lens = torch.full((S,), Lmax, dtype=torch.int32, device=self.keys.device)
+        self.seq_lens = _need(seq_lens, torch.int32, "seq_lens", 1)
+        self.S, self.Lmax, self.d, self.T, self.H = S, Lmax, d, T, H
+        self.c = MisaBatch(self.keys.data_ptr(), self.seq_lens.data_ptr(), self.q.data_ptr(),
+                           self.w.data_ptr(), self.q_seq.data_ptr(), self.q_pos.data_ptr(),
+                           S, Lmax, d, T, H)
+
+    @classmethod
+    def from_numpy(cls, case, device="cuda"):
+        """Upload a case from :mod:`synth` (bf16 bits as uint16)."""
+        torch = _torch()
+        import numpy as np
+
+        def bf(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+
+        def i32(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+        return cls(bf(case["keys"]), bf(case["q"]),
+                   torch.from_numpy(np.ascontiguousarray(case["w"], dtype=np.float32)).to(device),
+                   i32(case["q_seq"]), i32(case["q_pos"]), i32(case["seq_lens"]))
+
+    def workspace_bytes(self, op, B=1, h=1, k=1, kc=1):
+        n = _SZ(0)
+        _check(load().misa_workspace_bytes(ctypes.byref(self.c), op, B, h, k, kc, ctypes.byref(n)),
+               "misa_workspace_bytes")
+        return n.value
+
+    def workspace(self, op, B=1, h=1, k=1, kc=1):
+        torch = _torch()
+        return torch.empty(self.workspace_bytes(op, B, h, k, kc), dtype=torch.uint8,
+                           device=self.keys.device)
+
+
+def _ws(batch, ws, op, **kw):
+    if ws is None:
+        ws = batch.workspace(op, **kw)
+    return ws, _SZ(ws.numel() * ws.element_size())
+
+
+def pool(batch: Batch, B: int, out=None, stream=None):
+    torch = _torch()
+    M = (batch.Lmax + B - 1) // B
+    if out is None:
+        out = torch.empty((batch.S, M, batch.d), dtype=torch.float32, device=batch.keys.device)
+    _need(out, torch.float32, "pooled")
+    _check(load().misa_pool(ctypes.byref(batch.c), B, _ptr(out), _stream(stream)), "misa_pool")
+    return out
+
+
+def route(batch: Batch, pooled, B: int, h: int, mode: int = 0, heads=None, head_score=None,
+          want_score=False, ws=None, stream=None):
+    torch = _torch()
+    dev = batch.keys.device
+    if heads is None:
+        heads = torch.empty((batch.T, h), dtype=torch.int32, device=dev)
+    if head_score is None and want_score:
+        head_score = torch.empty((batch.T, batch.H), dtype=torch.float32, device=dev)
+    ws, nws = _ws(batch, ws, MISA_OP_ROUTE, B=B, h=h)
+    _check(load().misa_route(ctypes.byref(batch.c), _ptr(pooled), B, h, mode, _ptr(heads),
+                             _ptr(head_score), _ptr(ws), nws, _stream(stream)), "misa_route")
+    return (heads, head_score) if want_score or head_score is not None else heads
+
+
+def score(batch: Batch, heads=None, out=None, stream=None):
+    torch = _torch()
+    if out is None:
+        out = torch.empty((batch.T, batch.Lmax), dtype=torch.float32, device=batch.keys.device)
+    h = 0 if heads is None else heads.shape[1]
+    _check(load().misa_score(ctypes.byref(batch.c), _ptr(heads), h, _ptr(out), _stream(stream)),
+           "misa_score")
+    return out
+
+
+def _sel_out(batch_T, k, dev, idx, val, want_val):
+    torch = _torch()
+    if idx is None:
+        idx = torch.empty((batch_T, k), dtype=torch.int32, device=dev)
+    if val is None and want_val:
+        val = torch.empty((batch_T, k), dtype=torch.float32, device=dev)
+    return idx, val
+
+
+def score_topk(batch: Batch, heads, k: int, idx=None, val=None, want_val=True, ws=None, stream=None):
+    idx, val = _sel_out(batch.T, k, batch.keys.device, idx, val, want_val)
+    h = 0 if heads is None else heads.shape[1]
+    ws, nws = _ws(batch, ws, MISA_OP_SCORE_TOPK, h=max(h, 1), k=k)
+    _check(load().misa_score_topk(ctypes.byref(batch.c), _ptr(heads), h, k, _ptr(idx), _ptr(val),
+                                  _ptr(ws), nws, _stream(stream)), "misa_score_topk")
+    return idx, val
+
+
+def indexer_dense(batch: Batch, k: int, idx=None, val=None, want_val=True, ws=None, stream=None):
+    idx, val = _sel_out(batch.T, k, batch.keys.device, idx, val, want_val)
+    ws, nws = _ws(batch, ws, MISA_OP_DENSE, k=k)
+    _check(load().indexer_dense(ctypes.byref(batch.c), k, _ptr(idx), _ptr(val), _ptr(ws), nws,
+                                _stream(stream)), "indexer_dense")
+    return idx, val
+
+
+def rerank(batch: Batch, cand, k: int, idx=None, val=None, want_val=True, ws=None, stream=None):
+    torch = _torch()
+    _need(cand, torch.int32, "cand", 2)
+    kc = cand.shape[1]
+    idx, val = _sel_out(batch.T, k, batch.keys.device, idx, val, want_val)
+    ws, nws = _ws(batch, ws, MISA_OP_RERANK, k=k, kc=kc)
+    _check(load().misa_rerank(ctypes.byref(batch.c), _ptr(cand), kc, k, _ptr(idx), _ptr(val),
+                              _ptr(ws), nws, _stream(stream)), "misa_rerank")
+    return idx, val
+
+
+def topk(scores, row_len, k: int, idx=None, val=None, want_val=True, ws=None, stream=None):
+    torch = _torch()
+    _need(scores, torch.float32, "scores", 2)
+    _need(row_len, torch.int32, "row_len", 1)
+    rows, ld = scores.shape
+    idx, val = _sel_out(rows, k, scores.device, idx, val, want_val)
+    if ws is None:
+        shape = MisaBatch(1, 0, 0, 0, 0, 0, 1, ld, 128, rows, 1)
+        n = _SZ(0)
+        _check(load().misa_workspace_bytes(ctypes.byref(shape), MISA_OP_TOPK, 1, 1, k, 1,
+                                           ctypes.byref(n)), "misa_workspace_bytes")
+        ws = torch.empty(n.value, dtype=torch.uint8, device=scores.device)
+    _check(load().misa_topk(_ptr(scores), rows, ld, _ptr(row_len), k, _ptr(idx), _ptr(val),
+                            _ptr(ws), _SZ(ws.numel()), _stream(stream)), "misa_topk")
+    return idx, val

@@ -1,0 +1,288 @@
+// api.hip -- the C ABI (include/misa_indexer.h): argument validation,
+// workspace layout and kernel launch sequences.  Every check runs before
+// any HIP call; every call only enqueues work on the caller's stream.
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/misa_indexer.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace misa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kTopkCapMax = 16384;
+constexpr int kMaxRows = 65535;  // rows go on grid dimension y
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+int check_batch(const misa_batch *b, bool need_q) {
+  if (!b) return MISA_ERR_NULL;
+  if (!b->keys) return MISA_ERR_NULL;
+  if (need_q && (!b->q || !b->w || !b->q_seq || !b->q_pos)) return MISA_ERR_NULL;
+  if (b->d != MISA_D) return MISA_ERR_UNSUPPORTED;
+  if (b->S < 1 || b->Lmax < 1) return MISA_ERR_SHAPE;
+  if (need_q) {
+    if (b->T < 1 || b->H < 1) return MISA_ERR_SHAPE;
+    if (b->H > MISA_MAX_HEADS) return MISA_ERR_UNSUPPORTED;
+    if (b->T > kMaxRows) return MISA_ERR_UNSUPPORTED;
+  }
+  return MISA_OK;
+}
+
+// Layout of the selection workspace for `rows` score rows of `ld` columns.
+struct SelectLayout {
+  size_t scores, hist, counters, cand, total;
+  int cap;
+};
+SelectLayout select_layout(size_t rows, size_t ld, bool with_scores) {
+  SelectLayout L;
+  L.cap = (int)std::min<size_t>(ld, kTopkCapMax);
+  size_t off = 0;
+  L.scores = off;
+  if (with_scores) off = align_up(off + rows * ld * sizeof(float));
+  L.hist = off;
+  off = align_up(off + rows * kHistBins * sizeof(uint32_t));
+  L.counters = off;  // directly after the histogram: one fill clears both
+  off = align_up(off + rows * 4 * sizeof(uint32_t));
+  L.cand = off;
+  off = align_up(off + rows * (size_t)L.cap * sizeof(uint2));
+  L.total = off;
+  return L;
+}
+
+size_t route_bytes(const misa_batch *b, int B) {
+  const int Mmax = (b->Lmax + B - 1) / B;
+  const int nchunks = (Mmax + kRouteChunk - 1) / kRouteChunk;
+  return align_up((size_t)b->T * (nchunks + 1) * b->H * sizeof(float));
+}
+
+int score_chunk(int rows, int ncols) {
+  // about 2048 workgroups over the whole launch, 256..8192 columns each
+  const size_t work = (size_t)rows * ncols;
+  size_t c = (work + 2047) / 2048;
+  c = (c + 255) / 256 * 256;
+  c = std::max<size_t>(256, std::min<size_t>(8192, c));
+  return (int)c;
+}
+
+int filter_chunk(int rows, int ncols) {
+  const int per_row = std::max(1, 512 / std::max(1, rows));
+  int c = (ncols + per_row - 1) / per_row;
+  c = (c + 255) / 256 * 256;
+  return std::max(256, c);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MISA_OK : MISA_ERR_HIP; }
+
+// zero -> [score + histogram] -> filter -> finish, over rows of ld columns.
+int run_select(const ScoreArgs *score, const float *scores_in, int rows, int ld,
+               const int32_t *row_len, int row_len_add, const int32_t *map, int k,
+               int32_t *idx, float *val, void *ws, const SelectLayout &L, hipStream_t st) {
+  char *w = (char *)ws;
+  uint32_t *hist = (uint32_t *)(w + L.hist);
+  uint32_t *counters = (uint32_t *)(w + L.counters);
+  hipError_t e = launch_fill_u32(hist, (L.cand - L.hist) / sizeof(uint32_t), 0u, st);
+  if (e != hipSuccess) return MISA_ERR_HIP;
+  TopkArgs t{};
+  t.scores = score ? score->scores : scores_in;
+  t.row_len = row_len;
+  t.row_len_add = row_len_add;
+  t.map = map;
+  t.hist = hist;
+  t.counters = counters;
+  t.cand = (uint2 *)(w + L.cand);
+  t.cap = L.cap;
+  t.idx = idx;
+  t.val = val;
+  t.rows = rows;
+  t.ld = ld;
+  t.k = k;
+  if (score) {
+    ScoreArgs s = *score;
+    s.hist = hist;
+    e = launch_score_rows(s, st);
+  } else {
+    t.chunk = score_chunk(rows, ld);
+    e = launch_topk_hist(t, hist, st);
+  }
+  if (e != hipSuccess) return MISA_ERR_HIP;
+  t.chunk = filter_chunk(rows, ld);
+  if ((e = launch_topk_filter(t, st)) != hipSuccess) return MISA_ERR_HIP;
+  if ((e = launch_topk_finish(t, st)) != hipSuccess) return MISA_ERR_HIP;
+  return MISA_OK;
+}
+
+ScoreArgs make_score_args(const misa_batch *b, const int32_t *heads, int nh) {
+  ScoreArgs s{};
+  s.keys = b->keys;
+  s.q = b->q;
+  s.w = b->w;
+  s.q_seq = b->q_seq;
+  s.q_pos = b->q_pos;
+  s.heads = heads;
+  s.nh = nh;
+  s.H = b->H;
+  s.Lmax = b->Lmax;
+  s.T = b->T;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *misa_status_str(int status) {
+  switch (status) {
+    case MISA_OK: return "ok";
+    case MISA_ERR_NULL: return "a required pointer is NULL";
+    case MISA_ERR_SHAPE: return "a size or count is out of range";
+    case MISA_ERR_UNSUPPORTED: return "unsupported argument for this build";
+    case MISA_ERR_WORKSPACE: return "workspace is smaller than required";
+    case MISA_ERR_HIP: return "a HIP launch or runtime call failed";
+    default: return "unknown status";
+  }
+}
+
+int misa_workspace_bytes(const misa_batch *b, int32_t op, int32_t B, int32_t h, int32_t k,
+                         int32_t kc, size_t *bytes) {
+  if (!b || !bytes) return MISA_ERR_NULL;
+  if (b->d != MISA_D) return MISA_ERR_UNSUPPORTED;
+  if (b->S < 1 || b->Lmax < 1 || b->T < 1 || b->H < 1) return MISA_ERR_SHAPE;
+  switch (op) {
+    case MISA_OP_ROUTE:
+      if (B < 1 || B > b->Lmax || h < 1 || h > b->H) return MISA_ERR_SHAPE;
+      *bytes = route_bytes(b, B);
+      return MISA_OK;
+    case MISA_OP_DENSE:
+    case MISA_OP_SCORE_TOPK:
+      if (k < 1 || k > b->Lmax) return MISA_ERR_SHAPE;
+      *bytes = select_layout(b->T, b->Lmax, true).total;
+      return MISA_OK;
+    case MISA_OP_RERANK:
+      if (k < 1 || kc < k || kc > b->Lmax) return MISA_ERR_SHAPE;
+      *bytes = select_layout(b->T, kc, true).total;
+      return MISA_OK;
+    case MISA_OP_TOPK:
+      if (k < 1) return MISA_ERR_SHAPE;
+      *bytes = select_layout(b->T, b->Lmax, false).total;
+      return MISA_OK;
+    default:
+      return MISA_ERR_SHAPE;
+  }
+}
+
+int misa_pool(const misa_batch *b, int32_t B, float *pooled, void *stream) {
+  int rc = check_batch(b, false);
+  if (rc) return rc;
+  if (!b->seq_lens || !pooled) return MISA_ERR_NULL;
+  if (B < 1 || B > b->Lmax) return MISA_ERR_SHAPE;
+  if (b->S > kMaxRows) return MISA_ERR_UNSUPPORTED;
+  return hip_status(launch_pool(b->keys, b->seq_lens, b->S, b->Lmax, B, pooled,
+                                (hipStream_t)stream));
+}
+
+int misa_route(const misa_batch *b, const float *pooled, int32_t B, int32_t h, int32_t mode,
+               int32_t *heads, float *head_score, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_batch(b, true);
+  if (rc) return rc;
+  if (!pooled || !heads || !ws) return MISA_ERR_NULL;
+  if (B < 1 || B > b->Lmax || h < 1 || h > b->H) return MISA_ERR_SHAPE;
+  if (mode != 0 && mode != 1) return MISA_ERR_SHAPE;
+  if (ws_bytes < route_bytes(b, B)) return MISA_ERR_WORKSPACE;
+  RouteArgs a{};
+  a.keys = b->keys;
+  a.q = b->q;
+  a.w = b->w;
+  a.q_seq = b->q_seq;
+  a.q_pos = b->q_pos;
+  a.pooled = pooled;
+  a.partial = (float *)ws;
+  a.heads = heads;
+  a.g = head_score;
+  a.S = b->S;
+  a.Lmax = b->Lmax;
+  a.T = b->T;
+  a.H = b->H;
+  a.B = B;
+  a.h = h;
+  a.mode = mode;
+  a.Mmax = (b->Lmax + B - 1) / B;
+  a.nchunks = (a.Mmax + kRouteChunk - 1) / kRouteChunk;
+  return hip_status(launch_route(a, (hipStream_t)stream));
+}
+
+int misa_score(const misa_batch *b, const int32_t *heads, int32_t h, float *scores,
+               void *stream) {
+  int rc = check_batch(b, true);
+  if (rc) return rc;
+  if (!scores) return MISA_ERR_NULL;
+  if (heads && (h < 1 || h > b->H)) return MISA_ERR_SHAPE;
+  ScoreArgs s = make_score_args(b, heads, heads ? h : b->H);
+  s.scores = scores;
+  s.hist = nullptr;
+  s.cand = nullptr;
+  s.ncols = b->Lmax;
+  s.ld = b->Lmax;
+  s.chunk = score_chunk(b->T, b->Lmax);
+  return hip_status(launch_score_rows(s, (hipStream_t)stream));
+}
+
+int misa_topk(const float *scores, int32_t rows, int32_t ld, const int32_t *row_len, int32_t k,
+              int32_t *idx, float *val, void *ws, size_t ws_bytes, void *stream) {
+  if (!scores || !row_len || !idx || !ws) return MISA_ERR_NULL;
+  if (rows < 1 || ld < 1 || k < 1) return MISA_ERR_SHAPE;
+  if (rows > kMaxRows) return MISA_ERR_UNSUPPORTED;
+  const SelectLayout L = select_layout(rows, ld, false);
+  if (ws_bytes < L.total) return MISA_ERR_WORKSPACE;
+  return run_select(nullptr, scores, rows, ld, row_len, 0, nullptr, k, idx, val, ws, L,
+                    (hipStream_t)stream);
+}
+
+int misa_score_topk(const misa_batch *b, const int32_t *heads, int32_t h, int32_t k,
+                    int32_t *idx, float *val, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_batch(b, true);
+  if (rc) return rc;
+  if (!idx || !ws) return MISA_ERR_NULL;
+  if (heads && (h < 1 || h > b->H)) return MISA_ERR_SHAPE;
+  if (k < 1 || k > b->Lmax) return MISA_ERR_SHAPE;
+  const SelectLayout L = select_layout(b->T, b->Lmax, true);
+  if (ws_bytes < L.total) return MISA_ERR_WORKSPACE;
+  ScoreArgs s = make_score_args(b, heads, heads ? h : b->H);
+  s.scores = (float *)((char *)ws + L.scores);
+  s.cand = nullptr;
+  s.ncols = b->Lmax;
+  s.ld = b->Lmax;
+  s.chunk = score_chunk(b->T, b->Lmax);
+  return run_select(&s, nullptr, b->T, b->Lmax, b->q_pos, 1, nullptr, k, idx, val, ws, L,
+                    (hipStream_t)stream);
+}
+
+int indexer_dense(const misa_batch *b, int32_t k, int32_t *idx, float *val, void *ws,
+                  size_t ws_bytes, void *stream) {
+  return misa_score_topk(b, nullptr, 0, k, idx, val, ws, ws_bytes, stream);
+}
+
+int misa_rerank(const misa_batch *b, const int32_t *cand, int32_t kc, int32_t k, int32_t *idx,
+                float *val, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_batch(b, true);
+  if (rc) return rc;
+  if (!cand || !idx || !ws) return MISA_ERR_NULL;
+  if (k < 1 || kc < k || kc > b->Lmax) return MISA_ERR_SHAPE;
+  const SelectLayout L = select_layout(b->T, kc, true);
+  if (ws_bytes < L.total) return MISA_ERR_WORKSPACE;
+  ScoreArgs s = make_score_args(b, nullptr, b->H);
+  s.scores = (float *)((char *)ws + L.scores);
+  s.cand = cand;
+  s.ncols = kc;
+  s.ld = kc;
+  s.chunk = score_chunk(b->T, kc);
+  return run_select(&s, nullptr, b->T, kc, nullptr, 0, cand, k, idx, val, ws, L,
+                    (hipStream_t)stream);
+}
+
+}  // extern "C"

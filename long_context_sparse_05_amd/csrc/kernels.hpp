@@ -1,0 +1,65 @@
+// kernels.hpp -- argument blocks and host launchers of the gfx950 kernels.
+// Internal to the library: the public boundary is include/misa_indexer.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace misa {
+
+// Token scoring over score rows (score.hip).
+struct ScoreArgs {
+  const uint16_t *keys;    // bf16 [S][Lmax][128]
+  const uint16_t *q;       // bf16 [T][H][128]
+  const float *w;          // [T][H]
+  const int32_t *q_seq;    // [T]
+  const int32_t *q_pos;    // [T]
+  const int32_t *heads;    // [T][nh] or nullptr (rows 0..nh-1 = heads 0..nh-1)
+  const int32_t *cand;     // [T][ncols] token ids (-1 empty) or nullptr (column = token)
+  float *scores;           // [T][ld]
+  uint32_t *hist;          // [T][4096] first-digit histogram, or nullptr
+  int nh, H, Lmax, T;
+  int ncols, ld, chunk;
+};
+hipError_t launch_score_rows(const ScoreArgs &a, hipStream_t st);
+
+// Per-row top-k selection (topk.hip).
+struct TopkArgs {
+  const float *scores;     // [rows][ld]
+  const int32_t *row_len;  // [rows] or nullptr (all ld columns)
+  int row_len_add;         // valid columns = row_len[r] + row_len_add
+  const int32_t *map;      // [rows][ld] column -> token id (-1 = empty) or nullptr
+  const uint32_t *hist;    // [rows][4096] first-digit histogram of valid columns
+  uint32_t *counters;      // [rows][4]: selected-above count, candidate count
+  uint2 *cand;             // [rows][cap] (order key, column)
+  int cap;
+  int32_t *idx;            // [rows][k]
+  float *val;              // [rows][k] or nullptr
+  int rows, ld, k, chunk;
+};
+hipError_t launch_topk_hist(const TopkArgs &a, uint32_t *hist, hipStream_t st);
+hipError_t launch_topk_filter(const TopkArgs &a, hipStream_t st);
+hipError_t launch_topk_finish(const TopkArgs &a, hipStream_t st);
+hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t st);
+
+// Block mean-pool (pool.hip).
+hipError_t launch_pool(const uint16_t *keys, const int32_t *seq_lens, int S, int Lmax,
+                       int B, float *pooled, hipStream_t st);
+
+// Head router (route.hip).
+struct RouteArgs {
+  const uint16_t *keys;
+  const uint16_t *q;
+  const float *w;
+  const int32_t *q_seq;
+  const int32_t *q_pos;
+  const float *pooled;     // [S][Mmax][128]
+  float *partial;          // [T][nchunks + 1][H]
+  int32_t *heads;          // [T][h]
+  float *g;                // [T][H] or nullptr
+  int S, Lmax, T, H, B, h, mode, Mmax, nchunks;
+};
+constexpr int kRouteChunk = 64;  // complete blocks per router workgroup
+hipError_t launch_route(const RouteArgs &a, hipStream_t st);
+
+}  // namespace misa

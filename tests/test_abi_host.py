@@ -1,0 +1,120 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point include/misa_indexer.h declares, and rejects invalid
+arguments with the documented status before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_sparse_05_amd import abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "misa_indexer.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE = 0, -1, -2, -3, -4
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", src, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(abi.LIB_PATH):
+        from long_context_sparse_05_amd import build_lib
+        build_lib.build()
+    return abi.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(abi.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, -5):
+        assert abi.status_str(code) and abi.status_str(code) != "unknown status"
+    assert abi.status_str(12345) == "unknown status"
+
+
+FAKE = 0x1000  # a non-NULL pointer value; validation fails before it is used
+
+
+def batch(**kw):
+    f = dict(keys=FAKE, seq_lens=FAKE, q=FAKE, w=FAKE, q_seq=FAKE, q_pos=FAKE,
+             S=2, Lmax=4096, d=128, T=4, H=64)
+    f.update(kw)
+    return abi.MisaBatch(f["keys"], f["seq_lens"], f["q"], f["w"], f["q_seq"], f["q_pos"],
+                         f["S"], f["Lmax"], f["d"], f["T"], f["H"])
+
+
+def ws_bytes(lib, b, op, B=1, h=1, k=1, kc=1):
+    n = ctypes.c_size_t(0)
+    rc = lib.misa_workspace_bytes(ctypes.byref(b), op, B, h, k, kc, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_sizes(lib):
+    b = batch()
+    for op, kw in ((abi.MISA_OP_ROUTE, dict(B=64, h=8)), (abi.MISA_OP_SCORE_TOPK, dict(k=256)),
+                   (abi.MISA_OP_DENSE, dict(k=256)), (abi.MISA_OP_RERANK, dict(k=256, kc=1024)),
+                   (abi.MISA_OP_TOPK, dict(k=256))):
+        rc, n = ws_bytes(lib, b, op, **kw)
+        assert rc == OK and n > 0 and n % 256 == 0
+    # the score workspace holds at least the fp32 score rows
+    assert ws_bytes(lib, b, abi.MISA_OP_SCORE_TOPK, k=8)[1] >= 4 * 4096 * 4
+    assert ws_bytes(lib, b, 99)[0] == ERR_SHAPE
+    assert ws_bytes(lib, batch(d=64), abi.MISA_OP_DENSE, k=8)[0] == ERR_UNSUPPORTED
+    assert ws_bytes(lib, b, abi.MISA_OP_DENSE, k=0)[0] == ERR_SHAPE
+    assert ws_bytes(lib, b, abi.MISA_OP_DENSE, k=4097)[0] == ERR_SHAPE
+    assert ws_bytes(lib, b, abi.MISA_OP_RERANK, k=300, kc=200)[0] == ERR_SHAPE
+    assert ws_bytes(lib, b, abi.MISA_OP_ROUTE, B=64, h=65)[0] == ERR_SHAPE
+
+
+def test_validation_before_any_hip_call(lib):
+    P = ctypes.c_void_p
+    F = P(FAKE)
+    big = ctypes.c_size_t(1 << 40)
+    b = batch()
+    # NULL batch / pointers
+    assert lib.misa_pool(None, 64, F, None) == ERR_NULL
+    assert lib.misa_pool(ctypes.byref(batch(seq_lens=0)), 64, F, None) == ERR_NULL
+    assert lib.misa_pool(ctypes.byref(b), 64, None, None) == ERR_NULL
+    assert lib.misa_route(ctypes.byref(batch(q=0)), F, 64, 8, 0, F, None, F, big, None) == ERR_NULL
+    assert lib.misa_route(ctypes.byref(b), None, 64, 8, 0, F, None, F, big, None) == ERR_NULL
+    assert lib.misa_score_topk(ctypes.byref(b), None, 0, 8, None, None, F, big, None) == ERR_NULL
+    assert lib.indexer_dense(ctypes.byref(batch(keys=0)), 8, F, None, F, big, None) == ERR_NULL
+    assert lib.misa_rerank(ctypes.byref(b), None, 64, 8, F, None, F, big, None) == ERR_NULL
+    assert lib.misa_score(ctypes.byref(b), None, 0, None, None) == ERR_NULL
+    assert lib.misa_topk(None, 4, 64, F, 8, F, None, F, big, None) == ERR_NULL
+    # shapes
+    assert lib.misa_pool(ctypes.byref(b), 0, F, None) == ERR_SHAPE
+    assert lib.misa_pool(ctypes.byref(b), 4097, F, None) == ERR_SHAPE
+    assert lib.misa_pool(ctypes.byref(batch(d=64)), 64, F, None) == ERR_UNSUPPORTED
+    assert lib.misa_route(ctypes.byref(b), F, 64, 0, 0, F, None, F, big, None) == ERR_SHAPE
+    assert lib.misa_route(ctypes.byref(b), F, 64, 65, 0, F, None, F, big, None) == ERR_SHAPE
+    assert lib.misa_route(ctypes.byref(b), F, 64, 8, 2, F, None, F, big, None) == ERR_SHAPE
+    assert lib.misa_route(ctypes.byref(b), F, 0, 8, 0, F, None, F, big, None) == ERR_SHAPE
+    assert lib.misa_route(ctypes.byref(batch(H=0)), F, 64, 1, 0, F, None, F, big, None) == ERR_SHAPE
+    assert lib.misa_route(ctypes.byref(batch(H=129)), F, 64, 8, 0, F, None, F, big, None) == ERR_UNSUPPORTED
+    assert lib.misa_route(ctypes.byref(batch(T=0)), F, 64, 8, 0, F, None, F, big, None) == ERR_SHAPE
+    assert lib.misa_score_topk(ctypes.byref(b), F, 0, 8, F, None, F, big, None) == ERR_SHAPE
+    assert lib.misa_score_topk(ctypes.byref(b), F, 8, 0, F, None, F, big, None) == ERR_SHAPE
+    assert lib.misa_score_topk(ctypes.byref(b), F, 8, 4097, F, None, F, big, None) == ERR_SHAPE
+    assert lib.misa_rerank(ctypes.byref(b), F, 100, 101, F, None, F, big, None) == ERR_SHAPE
+    assert lib.misa_rerank(ctypes.byref(b), F, 5000, 8, F, None, F, big, None) == ERR_SHAPE
+    assert lib.misa_score(ctypes.byref(b), F, 65, F, None) == ERR_SHAPE
+    assert lib.misa_topk(F, 0, 64, F, 8, F, None, F, big, None) == ERR_SHAPE
+    assert lib.misa_topk(F, 4, 64, F, 0, F, None, F, big, None) == ERR_SHAPE
+    # workspace too small
+    small = ctypes.c_size_t(1024)
+    assert lib.misa_route(ctypes.byref(b), F, 64, 8, 0, F, None, F, small, None) == ERR_WORKSPACE
+    assert lib.misa_score_topk(ctypes.byref(b), F, 8, 64, F, None, F, small, None) == ERR_WORKSPACE
+    assert lib.indexer_dense(ctypes.byref(b), 64, F, None, F, small, None) == ERR_WORKSPACE
+    assert lib.misa_rerank(ctypes.byref(b), F, 128, 64, F, None, F, small, None) == ERR_WORKSPACE
+    assert lib.misa_topk(F, 4, 64, F, 8, F, None, F, small, None) == ERR_WORKSPACE
