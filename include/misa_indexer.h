@@ -96,6 +96,7 @@ typedef struct misa_batch {
 #define MISA_OP_SCORE_TOPK 2  /* misa_score_topk                      */
 #define MISA_OP_RERANK 3      /* misa_rerank                          */
 #define MISA_OP_TOPK 4        /* misa_topk (b->T rows of b->Lmax)     */
+#define MISA_OP_INDEXER 5     /* misa_indexer                         */
 
 /*
  * misa_workspace_bytes: device workspace needed by operation `op` for this
@@ -175,6 +176,18 @@ int misa_score_topk(const misa_batch *b, const int32_t *heads, int32_t h,
                     size_t ws_bytes, void *stream);
 
 /*
+ * misa_score_topk_ev -- misa_score_topk with a measurement hook: ev_start and
+ * ev_stop (hipEvent_t passed as void*, created by the caller; either may be
+ * NULL) are recorded on `stream` immediately before and after the
+ * token-scoring kernel, so hipEventElapsedTime(ev_start, ev_stop) is that
+ * kernel's duration.  Everything else is exactly misa_score_topk.
+ */
+int misa_score_topk_ev(const misa_batch *b, const int32_t *heads, int32_t h,
+                       int32_t k, int32_t *idx, float *val, void *ws,
+                       size_t ws_bytes, void *stream, void *ev_start,
+                       void *ev_stop);
+
+/*
  * indexer_dense -- the DSA lightning indexer: all H heads score every
  * prefix key, then the per-query top-k (Problem Statement).  Same outputs as
  * misa_score_topk with heads == NULL.  ws: MISA_OP_DENSE.
@@ -194,6 +207,30 @@ int indexer_dense(const misa_batch *b, int32_t k, int32_t *idx, float *val,
 int misa_rerank(const misa_batch *b, const int32_t *cand, int32_t kc, int32_t k,
                 int32_t *idx, float *val, void *ws, size_t ws_bytes,
                 void *stream);
+
+/*
+ * misa_indexer -- the whole MISA indexer step in one call: the router
+ * (exactly misa_route), then routed token scoring and the per-query top-k
+ * (exactly misa_score_topk with those heads) -- Methodology: MISA, both
+ * stages.  Outputs as the two calls: heads [T][h] (rank order), head_score
+ * [T][H] (may be NULL), idx/val [T][k].  One workspace (MISA_OP_INDEXER with
+ * B, h and k) holds both steps' scratch, so the router kernel can also clear
+ * the selection histogram and the step needs one launch less.
+ */
+int misa_indexer(const misa_batch *b, const float *pooled, int32_t B, int32_t h,
+                 int32_t mode, int32_t k, int32_t *heads, float *head_score,
+                 int32_t *idx, float *val, void *ws, size_t ws_bytes,
+                 void *stream);
+
+/*
+ * misa_indexer_ev -- misa_indexer with the measurement hook of
+ * misa_score_topk_ev (events around the token-scoring kernel).
+ */
+int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B,
+                    int32_t h, int32_t mode, int32_t k, int32_t *heads,
+                    float *head_score, int32_t *idx, float *val, void *ws,
+                    size_t ws_bytes, void *stream, void *ev_start,
+                    void *ev_stop);
 
 /* misa_status_str -- a static English description of a status code. */
 const char *misa_status_str(int status);

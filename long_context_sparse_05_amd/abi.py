@@ -17,11 +17,12 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmisa_indexer.so")
 
-MISA_OP_DENSE, MISA_OP_ROUTE, MISA_OP_SCORE_TOPK, MISA_OP_RERANK, MISA_OP_TOPK = range(5)
+MISA_OP_DENSE, MISA_OP_ROUTE, MISA_OP_SCORE_TOPK, MISA_OP_RERANK, MISA_OP_TOPK, MISA_OP_INDEXER = range(6)
 
 # Every entry point include/misa_indexer.h declares.
 EXPORTS = ("misa_workspace_bytes", "misa_pool", "misa_route", "misa_score", "misa_topk",
-           "misa_score_topk", "indexer_dense", "misa_rerank", "misa_status_str")
+           "misa_score_topk", "misa_score_topk_ev", "indexer_dense", "misa_rerank",
+           "misa_indexer", "misa_indexer_ev", "misa_status_str")
 
 
 class MisaBatch(ctypes.Structure):
@@ -53,8 +54,11 @@ def load():
         L.misa_score.argtypes = [BP, _P, _I, _P, _P]
         L.misa_topk.argtypes = [_P, _I, _I, _P, _I, _P, _P, _P, _SZ, _P]
         L.misa_score_topk.argtypes = [BP, _P, _I, _I, _P, _P, _P, _SZ, _P]
+        L.misa_score_topk_ev.argtypes = [BP, _P, _I, _I, _P, _P, _P, _SZ, _P, _P, _P]
         L.indexer_dense.argtypes = [BP, _I, _P, _P, _P, _SZ, _P]
         L.misa_rerank.argtypes = [BP, _P, _I, _I, _P, _P, _P, _SZ, _P]
+        L.misa_indexer.argtypes = [BP, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]
+        L.misa_indexer_ev.argtypes = [BP, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]
         for name in EXPORTS:
             getattr(L, name).restype = ctypes.c_int
         L.misa_status_str.argtypes = [ctypes.c_int]
@@ -199,12 +203,22 @@ def _sel_out(batch_T, k, dev, idx, val, want_val):
     return idx, val
 
 
-def score_topk(batch: Batch, heads, k: int, idx=None, val=None, want_val=True, ws=None, stream=None):
+def score_topk(batch: Batch, heads, k: int, idx=None, val=None, want_val=True, ws=None,
+               stream=None, events=None):
+    """misa_score_topk; `events` = (start, stop) raw hipEvent_t handles (ints)
+    recorded around the scoring kernel (misa_score_topk_ev)."""
     idx, val = _sel_out(batch.T, k, batch.keys.device, idx, val, want_val)
     h = 0 if heads is None else heads.shape[1]
     ws, nws = _ws(batch, ws, MISA_OP_SCORE_TOPK, h=max(h, 1), k=k)
-    _check(load().misa_score_topk(ctypes.byref(batch.c), _ptr(heads), h, k, _ptr(idx), _ptr(val),
-                                  _ptr(ws), nws, _stream(stream)), "misa_score_topk")
+    if events is None:
+        _check(load().misa_score_topk(ctypes.byref(batch.c), _ptr(heads), h, k, _ptr(idx),
+                                      _ptr(val), _ptr(ws), nws, _stream(stream)),
+               "misa_score_topk")
+    else:
+        _check(load().misa_score_topk_ev(ctypes.byref(batch.c), _ptr(heads), h, k, _ptr(idx),
+                                         _ptr(val), _ptr(ws), nws, _stream(stream),
+                                         ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1])),
+               "misa_score_topk_ev")
     return idx, val
 
 
@@ -214,6 +228,29 @@ def indexer_dense(batch: Batch, k: int, idx=None, val=None, want_val=True, ws=No
     _check(load().indexer_dense(ctypes.byref(batch.c), k, _ptr(idx), _ptr(val), _ptr(ws), nws,
                                 _stream(stream)), "indexer_dense")
     return idx, val
+
+
+def indexer(batch: Batch, pooled, B: int, h: int, k: int, mode: int = 0, heads=None,
+            head_score=None, idx=None, val=None, want_val=True, ws=None, stream=None,
+            events=None):
+    """misa_indexer: router + routed scoring + top-k in one call.
+    Returns (heads, idx, val)."""
+    torch = _torch()
+    dev = batch.keys.device
+    if heads is None:
+        heads = torch.empty((batch.T, h), dtype=torch.int32, device=dev)
+    idx, val = _sel_out(batch.T, k, dev, idx, val, want_val)
+    ws, nws = _ws(batch, ws, MISA_OP_INDEXER, B=B, h=h, k=k)
+    if events is None:
+        _check(load().misa_indexer(ctypes.byref(batch.c), _ptr(pooled), B, h, mode, k, _ptr(heads),
+                                   _ptr(head_score), _ptr(idx), _ptr(val), _ptr(ws), nws,
+                                   _stream(stream)), "misa_indexer")
+    else:
+        _check(load().misa_indexer_ev(ctypes.byref(batch.c), _ptr(pooled), B, h, mode, k,
+                                      _ptr(heads), _ptr(head_score), _ptr(idx), _ptr(val),
+                                      _ptr(ws), nws, _stream(stream), ctypes.c_void_p(events[0]),
+                                      ctypes.c_void_p(events[1])), "misa_indexer_ev")
+    return heads, idx, val
 
 
 def rerank(batch: Batch, cand, k: int, idx=None, val=None, want_val=True, ws=None, stream=None):

@@ -9,13 +9,13 @@
 #include "../../include/misa_indexer.h"
 #include "common.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 using namespace misa;
 
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kTopkCapMax = 16384;
 constexpr int kMaxRows = 65535;  // rows go on grid dimension y
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
@@ -34,21 +34,33 @@ int check_batch(const misa_batch *b, bool need_q) {
   return MISA_OK;
 }
 
-// Layout of the selection workspace for `rows` score rows of `ld` columns.
+int filter_chunk(int rows, int ncols) {
+  // about 512 filter workgroups, each a multiple of 4096 columns (one round)
+  const int per_row = std::max(1, 512 / std::max(1, rows));
+  int c = (ncols + per_row - 1) / per_row;
+  c = (c + 4095) / 4096 * 4096;
+  return std::max(4096, c);
+}
+
+// Layout of the selection workspace for `rows` score rows of `ld` columns:
+// fp32 score rows (when the call computes them), the first-digit histograms
+// and per-row counters (zeroed together by the call), and the per-row
+// threshold-digit candidate lists.
 struct SelectLayout {
   size_t scores, hist, counters, cand, total;
   int cap;
 };
-SelectLayout select_layout(size_t rows, size_t ld, bool with_scores) {
+SelectLayout select_layout(size_t rows, size_t ld, int k, bool with_scores) {
+  (void)k;
   SelectLayout L;
-  L.cap = (int)std::min<size_t>(ld, kTopkCapMax);
+  L.cap = (int)std::min<size_t>(ld, 16384);
   size_t off = 0;
   L.scores = off;
   if (with_scores) off = align_up(off + rows * ld * sizeof(float));
   L.hist = off;
   off = align_up(off + rows * kHistBins * sizeof(uint32_t));
-  L.counters = off;  // directly after the histogram: one fill clears both
-  off = align_up(off + rows * 4 * sizeof(uint32_t));
+  L.counters = off;  // directly after the histograms: one fill clears both
+  off = align_up(off + rows * kRowCounters * sizeof(uint32_t));
   L.cand = off;
   off = align_up(off + rows * (size_t)L.cap * sizeof(uint2));
   L.total = off;
@@ -62,41 +74,36 @@ size_t route_bytes(const misa_batch *b, int B) {
 }
 
 int score_chunk(int rows, int ncols) {
-  // about 2048 workgroups over the whole launch, 256..8192 columns each
+  // about 512 workgroups over the whole launch (two per CU), 256..4096 columns each
   const size_t work = (size_t)rows * ncols;
-  size_t c = (work + 2047) / 2048;
+  size_t c = (work + 511) / 512;
   c = (c + 255) / 256 * 256;
-  c = std::max<size_t>(256, std::min<size_t>(8192, c));
+  c = std::max<size_t>(256, std::min<size_t>(4096, c));
   return (int)c;
-}
-
-int filter_chunk(int rows, int ncols) {
-  const int per_row = std::max(1, 512 / std::max(1, rows));
-  int c = (ncols + per_row - 1) / per_row;
-  c = (c + 255) / 256 * 256;
-  return std::max(256, c);
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MISA_OK : MISA_ERR_HIP; }
 
-// zero -> [score + histogram] -> filter -> finish, over rows of ld columns.
+// zero the histograms -> [score rows + histogram | histogram] -> select.
 int run_select(const ScoreArgs *score, const float *scores_in, int rows, int ld,
                const int32_t *row_len, int row_len_add, const int32_t *map, int k,
-               int32_t *idx, float *val, void *ws, const SelectLayout &L, hipStream_t st) {
-  char *w = (char *)ws;
-  uint32_t *hist = (uint32_t *)(w + L.hist);
-  uint32_t *counters = (uint32_t *)(w + L.counters);
-  hipError_t e = launch_fill_u32(hist, (L.cand - L.hist) / sizeof(uint32_t), 0u, st);
-  if (e != hipSuccess) return MISA_ERR_HIP;
+               int32_t *idx, float *val, void *ws, const SelectLayout &L, hipStream_t st,
+               void *ev_start = nullptr, void *ev_stop = nullptr, bool zeroed = false) {
+  uint32_t *hist = (uint32_t *)((char *)ws + L.hist);
+  hipError_t e = hipSuccess;
+  if (!zeroed) {  // the fused indexer call clears these in its router kernel
+    e = launch_fill_u32(hist, (L.cand - L.hist) / sizeof(uint32_t), 0u, st);
+    if (e != hipSuccess) return MISA_ERR_HIP;
+  }
   TopkArgs t{};
+  t.counters = (uint32_t *)((char *)ws + L.counters);
+  t.cand = (uint2 *)((char *)ws + L.cand);
+  t.cap = L.cap;
   t.scores = score ? score->scores : scores_in;
   t.row_len = row_len;
   t.row_len_add = row_len_add;
   t.map = map;
   t.hist = hist;
-  t.counters = counters;
-  t.cand = (uint2 *)(w + L.cand);
-  t.cap = L.cap;
   t.idx = idx;
   t.val = val;
   t.rows = rows;
@@ -105,15 +112,16 @@ int run_select(const ScoreArgs *score, const float *scores_in, int rows, int ld,
   if (score) {
     ScoreArgs s = *score;
     s.hist = hist;
+    if (ev_start && hipEventRecord((hipEvent_t)ev_start, st) != hipSuccess) return MISA_ERR_HIP;
     e = launch_score_rows(s, st);
+    if (e == hipSuccess && ev_stop) e = hipEventRecord((hipEvent_t)ev_stop, st);
   } else {
     t.chunk = score_chunk(rows, ld);
     e = launch_topk_hist(t, hist, st);
   }
   if (e != hipSuccess) return MISA_ERR_HIP;
   t.chunk = filter_chunk(rows, ld);
-  if ((e = launch_topk_filter(t, st)) != hipSuccess) return MISA_ERR_HIP;
-  if ((e = launch_topk_finish(t, st)) != hipSuccess) return MISA_ERR_HIP;
+  if ((e = launch_topk_select(t, st)) != hipSuccess) return MISA_ERR_HIP;
   return MISA_OK;
 }
 
@@ -161,15 +169,19 @@ int misa_workspace_bytes(const misa_batch *b, int32_t op, int32_t B, int32_t h, 
     case MISA_OP_DENSE:
     case MISA_OP_SCORE_TOPK:
       if (k < 1 || k > b->Lmax) return MISA_ERR_SHAPE;
-      *bytes = select_layout(b->T, b->Lmax, true).total;
+      *bytes = select_layout(b->T, b->Lmax, k, true).total;
       return MISA_OK;
     case MISA_OP_RERANK:
       if (k < 1 || kc < k || kc > b->Lmax) return MISA_ERR_SHAPE;
-      *bytes = select_layout(b->T, kc, true).total;
+      *bytes = select_layout(b->T, kc, k, true).total;
+      return MISA_OK;
+    case MISA_OP_INDEXER:
+      if (B < 1 || B > b->Lmax || h < 1 || h > b->H || k < 1 || k > b->Lmax) return MISA_ERR_SHAPE;
+      *bytes = route_bytes(b, B) + select_layout(b->T, b->Lmax, k, true).total;
       return MISA_OK;
     case MISA_OP_TOPK:
       if (k < 1) return MISA_ERR_SHAPE;
-      *bytes = select_layout(b->T, b->Lmax, false).total;
+      *bytes = select_layout(b->T, b->Lmax, k, false).total;
       return MISA_OK;
     default:
       return MISA_ERR_SHAPE;
@@ -186,14 +198,8 @@ int misa_pool(const misa_batch *b, int32_t B, float *pooled, void *stream) {
                                 (hipStream_t)stream));
 }
 
-int misa_route(const misa_batch *b, const float *pooled, int32_t B, int32_t h, int32_t mode,
-               int32_t *heads, float *head_score, void *ws, size_t ws_bytes, void *stream) {
-  int rc = check_batch(b, true);
-  if (rc) return rc;
-  if (!pooled || !heads || !ws) return MISA_ERR_NULL;
-  if (B < 1 || B > b->Lmax || h < 1 || h > b->H) return MISA_ERR_SHAPE;
-  if (mode != 0 && mode != 1) return MISA_ERR_SHAPE;
-  if (ws_bytes < route_bytes(b, B)) return MISA_ERR_WORKSPACE;
+static RouteArgs make_route_args(const misa_batch *b, const float *pooled, int32_t B, int32_t h,
+                                 int32_t mode, int32_t *heads, float *head_score, void *ws) {
   RouteArgs a{};
   a.keys = b->keys;
   a.q = b->q;
@@ -213,6 +219,18 @@ int misa_route(const misa_batch *b, const float *pooled, int32_t B, int32_t h, i
   a.mode = mode;
   a.Mmax = (b->Lmax + B - 1) / B;
   a.nchunks = (a.Mmax + kRouteChunk - 1) / kRouteChunk;
+  return a;
+}
+
+int misa_route(const misa_batch *b, const float *pooled, int32_t B, int32_t h, int32_t mode,
+               int32_t *heads, float *head_score, void *ws, size_t ws_bytes, void *stream) {
+  int rc = check_batch(b, true);
+  if (rc) return rc;
+  if (!pooled || !heads || !ws) return MISA_ERR_NULL;
+  if (B < 1 || B > b->Lmax || h < 1 || h > b->H) return MISA_ERR_SHAPE;
+  if (mode != 0 && mode != 1) return MISA_ERR_SHAPE;
+  if (ws_bytes < route_bytes(b, B)) return MISA_ERR_WORKSPACE;
+  const RouteArgs a = make_route_args(b, pooled, B, h, mode, heads, head_score, ws);
   return hip_status(launch_route(a, (hipStream_t)stream));
 }
 
@@ -237,20 +255,21 @@ int misa_topk(const float *scores, int32_t rows, int32_t ld, const int32_t *row_
   if (!scores || !row_len || !idx || !ws) return MISA_ERR_NULL;
   if (rows < 1 || ld < 1 || k < 1) return MISA_ERR_SHAPE;
   if (rows > kMaxRows) return MISA_ERR_UNSUPPORTED;
-  const SelectLayout L = select_layout(rows, ld, false);
+  const SelectLayout L = select_layout(rows, ld, k, false);
   if (ws_bytes < L.total) return MISA_ERR_WORKSPACE;
   return run_select(nullptr, scores, rows, ld, row_len, 0, nullptr, k, idx, val, ws, L,
                     (hipStream_t)stream);
 }
 
-int misa_score_topk(const misa_batch *b, const int32_t *heads, int32_t h, int32_t k,
-                    int32_t *idx, float *val, void *ws, size_t ws_bytes, void *stream) {
+int misa_score_topk_ev(const misa_batch *b, const int32_t *heads, int32_t h, int32_t k,
+                       int32_t *idx, float *val, void *ws, size_t ws_bytes, void *stream,
+                       void *ev_start, void *ev_stop) {
   int rc = check_batch(b, true);
   if (rc) return rc;
   if (!idx || !ws) return MISA_ERR_NULL;
   if (heads && (h < 1 || h > b->H)) return MISA_ERR_SHAPE;
   if (k < 1 || k > b->Lmax) return MISA_ERR_SHAPE;
-  const SelectLayout L = select_layout(b->T, b->Lmax, true);
+  const SelectLayout L = select_layout(b->T, b->Lmax, k, true);
   if (ws_bytes < L.total) return MISA_ERR_WORKSPACE;
   ScoreArgs s = make_score_args(b, heads, heads ? h : b->H);
   s.scores = (float *)((char *)ws + L.scores);
@@ -259,12 +278,51 @@ int misa_score_topk(const misa_batch *b, const int32_t *heads, int32_t h, int32_
   s.ld = b->Lmax;
   s.chunk = score_chunk(b->T, b->Lmax);
   return run_select(&s, nullptr, b->T, b->Lmax, b->q_pos, 1, nullptr, k, idx, val, ws, L,
-                    (hipStream_t)stream);
+                    (hipStream_t)stream, ev_start, ev_stop);
+}
+
+int misa_score_topk(const misa_batch *b, const int32_t *heads, int32_t h, int32_t k,
+                    int32_t *idx, float *val, void *ws, size_t ws_bytes, void *stream) {
+  return misa_score_topk_ev(b, heads, h, k, idx, val, ws, ws_bytes, stream, nullptr, nullptr);
 }
 
 int indexer_dense(const misa_batch *b, int32_t k, int32_t *idx, float *val, void *ws,
                   size_t ws_bytes, void *stream) {
   return misa_score_topk(b, nullptr, 0, k, idx, val, ws, ws_bytes, stream);
+}
+
+int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t h, int32_t mode,
+                    int32_t k, int32_t *heads, float *head_score, int32_t *idx, float *val,
+                    void *ws, size_t ws_bytes, void *stream, void *ev_start, void *ev_stop) {
+  int rc = check_batch(b, true);
+  if (rc) return rc;
+  if (!pooled || !heads || !idx || !ws) return MISA_ERR_NULL;
+  if (B < 1 || B > b->Lmax || h < 1 || h > b->H) return MISA_ERR_SHAPE;
+  if (mode != 0 && mode != 1) return MISA_ERR_SHAPE;
+  if (k < 1 || k > b->Lmax) return MISA_ERR_SHAPE;
+  const size_t rbytes = route_bytes(b, B);
+  const SelectLayout L = select_layout(b->T, b->Lmax, k, true);
+  if (ws_bytes < rbytes + L.total) return MISA_ERR_WORKSPACE;
+  void *sws = (char *)ws + rbytes;
+  RouteArgs ra = make_route_args(b, pooled, B, h, mode, heads, head_score, ws);
+  ra.zero_hist = (uint32_t *)((char *)sws + L.hist);
+  ra.zero_ctr = (uint32_t *)((char *)sws + L.counters);
+  if (launch_route(ra, (hipStream_t)stream) != hipSuccess) return MISA_ERR_HIP;
+  ScoreArgs s = make_score_args(b, heads, h);
+  s.scores = (float *)((char *)sws + L.scores);
+  s.cand = nullptr;
+  s.ncols = b->Lmax;
+  s.ld = b->Lmax;
+  s.chunk = score_chunk(b->T, b->Lmax);
+  return run_select(&s, nullptr, b->T, b->Lmax, b->q_pos, 1, nullptr, k, idx, val, sws, L,
+                    (hipStream_t)stream, ev_start, ev_stop, true);
+}
+
+int misa_indexer(const misa_batch *b, const float *pooled, int32_t B, int32_t h, int32_t mode,
+                 int32_t k, int32_t *heads, float *head_score, int32_t *idx, float *val, void *ws,
+                 size_t ws_bytes, void *stream) {
+  return misa_indexer_ev(b, pooled, B, h, mode, k, heads, head_score, idx, val, ws, ws_bytes,
+                         stream, nullptr, nullptr);
 }
 
 int misa_rerank(const misa_batch *b, const int32_t *cand, int32_t kc, int32_t k, int32_t *idx,
@@ -273,7 +331,7 @@ int misa_rerank(const misa_batch *b, const int32_t *cand, int32_t kc, int32_t k,
   if (rc) return rc;
   if (!cand || !idx || !ws) return MISA_ERR_NULL;
   if (k < 1 || kc < k || kc > b->Lmax) return MISA_ERR_SHAPE;
-  const SelectLayout L = select_layout(b->T, kc, true);
+  const SelectLayout L = select_layout(b->T, kc, k, true);
   if (ws_bytes < L.total) return MISA_ERR_WORKSPACE;
   ScoreArgs s = make_score_args(b, nullptr, b->H);
   s.scores = (float *)((char *)ws + L.scores);

@@ -17,12 +17,21 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;          // key dimension
+#define MISA_MAX_HEADS_DEV 128   // largest H the kernels are built for
 constexpr int kWave = 64;        // wavefront width on CDNA
 constexpr int kHistBits = 12;    // first radix digit: top 12 bits of the key
 constexpr int kHistBins = 1 << kHistBits;
 constexpr int kHistShift = 32 - kHistBits;
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+// 16-byte load marked non-temporal: streamed data that is read once should
+// not displace reused lines from the caches.
+__device__ __forceinline__ uint4 load_nt16(const void *p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4 *)p);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -58,6 +67,16 @@ __device__ __forceinline__ void split3(float x, uint16_t &hi, uint16_t &mid, uin
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Sum over the 16 lanes of each DPP row (lanes 16r .. 16r+15), on the vector
+// ALU with row rotations (no LDS round trip); every lane gets its row's sum.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false));
+  return v;
+}
 
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {

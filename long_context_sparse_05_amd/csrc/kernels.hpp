@@ -17,7 +17,7 @@ struct ScoreArgs {
   const int32_t *heads;    // [T][nh] or nullptr (rows 0..nh-1 = heads 0..nh-1)
   const int32_t *cand;     // [T][ncols] token ids (-1 empty) or nullptr (column = token)
   float *scores;           // [T][ld]
-  uint32_t *hist;          // [T][4096] first-digit histogram, or nullptr
+  uint32_t *hist;          // [T][4096] first-digit histogram (accumulated), or nullptr
   int nh, H, Lmax, T;
   int ncols, ld, chunk;
 };
@@ -29,17 +29,16 @@ struct TopkArgs {
   const int32_t *row_len;  // [rows] or nullptr (all ld columns)
   int row_len_add;         // valid columns = row_len[r] + row_len_add
   const int32_t *map;      // [rows][ld] column -> token id (-1 = empty) or nullptr
-  const uint32_t *hist;    // [rows][4096] first-digit histogram of valid columns
-  uint32_t *counters;      // [rows][4]: selected-above count, candidate count
-  uint2 *cand;             // [rows][cap] (order key, column)
-  int cap;
+  const uint32_t *hist;    // [rows][4096] first-digit histogram of the valid columns
+  uint32_t *counters;      // [rows][kRowCounters] (select.hpp)
+  uint2 *cand;             // [rows][cap] threshold-digit candidates (order key, column)
+  int cap;                 // <= 16384
   int32_t *idx;            // [rows][k]
   float *val;              // [rows][k] or nullptr
-  int rows, ld, k, chunk;
+  int rows, ld, k, chunk;  // chunk: columns per workgroup (histogram / filter)
 };
 hipError_t launch_topk_hist(const TopkArgs &a, uint32_t *hist, hipStream_t st);
-hipError_t launch_topk_filter(const TopkArgs &a, hipStream_t st);
-hipError_t launch_topk_finish(const TopkArgs &a, hipStream_t st);
+hipError_t launch_topk_select(const TopkArgs &a, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t st);
 
 // Block mean-pool (pool.hip).
@@ -57,6 +56,8 @@ struct RouteArgs {
   float *partial;          // [T][nchunks + 1][H]
   int32_t *heads;          // [T][h]
   float *g;                // [T][H] or nullptr
+  uint32_t *zero_hist;     // [T][4096] zeroed by route_final (fused indexer call), or nullptr
+  uint32_t *zero_ctr;      // [T][8] zeroed with it
   int S, Lmax, T, H, B, h, mode, Mmax, nchunks;
 };
 constexpr int kRouteChunk = 64;  // complete blocks per router workgroup

@@ -26,7 +26,7 @@ namespace misa {
 template <int HT>
 __global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a) {
   __shared__ float part[4][HT * 16];
-  __shared__ float red[2][kD];
+  __shared__ float red[4][kD];
   __shared__ float mean[kD];
   const int t = blockIdx.y, ch = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -37,20 +37,76 @@ __global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a) {
   float *out = a.partial + ((size_t)t * (a.nchunks + 1) + ch) * a.H;
 
   if (ch == a.nchunks) {  // the query's own last block: [bt*B, p]
+    // Mean of the tail keys.  Thread = (8-dim slice dc, key lane kl): 16 key
+    // lanes stream the block with 16-byte loads; the 4 key lanes of a wave
+    // are folded with xor shuffles, the 4 waves through LDS.
     const int lo = bt * a.B;
-    const int c = tid & (kD - 1), half = tid >> 7;
-    const uint16_t *kb = a.keys + (size_t)sq * a.Lmax * kD + c;
-    float s = 0.f;
-    for (int i = lo + half; i <= p; i += 2) s += bf16_to_f32(kb[(size_t)i * kD]);
-    red[half][c] = s;
+    const int dc = tid & 15, kl = tid >> 4;
+    // this thread's query slices for the head dots below, requested first:
+    // thread = (head j = tid/4 + 64*round, 32-dim quarter qq)
+    const int qq = tid & 3;
+    uint4 qv[2][4];
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int j = rd * 64 + (tid >> 2);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        qv[rd][u] = j < a.H ? ((const uint4 *)(a.q + ((size_t)t * a.H + j) * kD + qq * 32))[u]
+                            : make_uint4(0, 0, 0, 0);
+    }
+    const uint16_t *kb = a.keys + (size_t)sq * a.Lmax * kD + dc * 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int i0 = lo + kl; i0 <= p; i0 += 16 * 8) {  // 8 loads in flight per thread
+      uint4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + 16 * u;
+        v[u] = i <= p ? *(const uint4 *)(kb + (size_t)i * kD) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += __uint_as_float(x[e] << 16);
+          acc[2 * e + 1] += __uint_as_float(x[e] & 0xFFFF0000u);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[e] += __shfl_xor(acc[e], 16, kWave);
+      acc[e] += __shfl_xor(acc[e], 32, kWave);
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[wave][dc * 8 + e] = acc[e];
+    }
     __syncthreads();
-    if (tid < kD) mean[tid] = (red[0][tid] + red[1][tid]) / (float)(p - lo + 1);
+    if (tid < kD)
+      mean[tid] = (((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid]) / (float)(p - lo + 1);
     __syncthreads();
-    for (int j = tid; j < a.H; j += 256) {
-      const uint16_t *qj = a.q + ((size_t)t * a.H + j) * kD;
+    // Head dots against the tail mean: thread = (head j, 32-dim quarter).
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int j = rd * 64 + (tid >> 2);
       float x = 0.f;
-      for (int cc = 0; cc < kD; ++cc) x = fmaf(bf16_to_f32(qj[cc]), mean[cc], x);
-      out[j] = fmaxf(x, 0.f);
+      if (j < a.H) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint4 v = qv[rd][u];
+          const uint32_t y[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int c = qq * 32 + u * 8 + 2 * e;
+            x = fmaf(__uint_as_float(y[e] << 16), mean[c], x);
+            x = fmaf(__uint_as_float(y[e] & 0xFFFF0000u), mean[c + 1], x);
+          }
+        }
+      }
+      x += __shfl_xor(x, 1, kWave);
+      x += __shfl_xor(x, 2, kWave);
+      if (j < a.H && qq == 0) out[j] = fmaxf(x, 0.f);
     }
     return;
   }
@@ -110,11 +166,7 @@ __global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a) {
   for (int ht = 0; ht < HT; ++ht) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float v = ok ? fmaxf(acc[ht][r], 0.f) : 0.f;
-      v += __shfl_xor(v, 1, kWave);
-      v += __shfl_xor(v, 2, kWave);
-      v += __shfl_xor(v, 4, kWave);
-      v += __shfl_xor(v, 8, kWave);
+      const float v = row_sum16(ok ? fmaxf(acc[ht][r], 0.f) : 0.f);
       if (col == 0) part[wave][ht * 16 + grp * 4 + r] = v;
     }
   }
@@ -122,53 +174,60 @@ __global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a) {
   for (int j = tid; j < a.H; j += 256) out[j] = ((part[0][j] + part[1][j]) + part[2][j]) + part[3][j];
 }
 
-__global__ __launch_bounds__(64) void route_final_kernel(RouteArgs a) {
+// One workgroup per query: four thread quarters sum contiguous quarters of
+// the partials (loads in flight together), combined in a fixed order; then
+// every head computes its own rank, and ranks below h are written.  In the
+// fused indexer call it also clears the query's selection histogram, which
+// saves the scoring step a separate fill launch.
+__global__ __launch_bounds__(256) void route_final_kernel(RouteArgs a) {
+  __shared__ float red[4][MISA_MAX_HEADS_DEV];
+  __shared__ float gs[MISA_MAX_HEADS_DEV];
   const int t = blockIdx.x;
-  const int lane = lane_id();
-  const float *pp = a.partial + (size_t)t * (a.nchunks + 1) * a.H;
-  float gv[2];
-  bool avail[2];
+  const int tid = threadIdx.x, lane = lane_id(), quarter = tid >> 6;
+  const int nparts = a.nchunks + 1;
+  const float *pp = a.partial + (size_t)t * nparts * a.H;
+  const int per = (nparts + 3) / 4;
+  const int c0 = quarter * per, c1 = min(nparts, c0 + per);
+  if (a.zero_hist) {  // fused indexer call: clear this query's selection histogram
+    uint4 *zh = (uint4 *)(a.zero_hist + (size_t)t * kHistBins);
+    for (int i = tid; i < kHistBins / 4; i += 256) zh[i] = make_uint4(0, 0, 0, 0);
+    if (tid < 8) a.zero_ctr[(size_t)t * 8 + tid] = 0u;
+  }
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int j = lane + 64 * u;
-    avail[u] = j < a.H;
-    gv[u] = 0.f;
-    if (avail[u]) {
+    if (j < a.H) {
       float s = 0.f;
-      for (int c = 0; c <= a.nchunks; ++c) s += pp[(size_t)c * a.H + j];
-      float wj = a.w[(size_t)t * a.H + j];
-      if (a.mode == 1) wj = fabsf(wj);
-      gv[u] = wj * s;
-      if (a.g) a.g[(size_t)t * a.H + j] = gv[u];
+      int c = c0;
+      for (; c + 8 <= c1; c += 8) {
+        float v[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) v[x] = pp[(size_t)(c + x) * a.H + j];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) s += v[x];
+      }
+      for (; c < c1; ++c) s += pp[(size_t)c * a.H + j];
+      red[quarter][j] = s;
     }
   }
-  for (int r = 0; r < a.h; ++r) {
-    // this lane's best remaining head under (g desc, id asc)
-    float bg = 0.f;
-    int bj = 0x7FFFFFFF;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int j = lane + 64 * u;
-      if (avail[u] && (bj == 0x7FFFFFFF || gv[u] > bg)) {
-        bg = gv[u];
-        bj = j;
-      }
+  __syncthreads();
+  if (tid < a.H) {
+    const float s = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    float wj = a.w[(size_t)t * a.H + tid];
+    if (a.mode == 1) wj = fabsf(wj);
+    gs[tid] = wj * s;
+    if (a.g) a.g[(size_t)t * a.H + tid] = gs[tid];
+  }
+  __syncthreads();
+  // rank of head j under (g desc, id asc); the heads of rank < h are routed
+  if (tid < a.H) {
+    const float gj = gs[tid];
+    int rank = 0;
+    for (int i = 0; i < a.H; ++i) {
+      const float gi = gs[i];
+      rank += (gi > gj || (gi == gj && i < tid)) ? 1 : 0;
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float og = __shfl_xor(bg, o, kWave);
-      const int oj = __shfl_xor(bj, o, kWave);
-      const bool better = oj != 0x7FFFFFFF &&
-                          (bj == 0x7FFFFFFF || og > bg || (!(og < bg) && oj < bj));
-      if (better) {
-        bg = og;
-        bj = oj;
-      }
-    }
-    if (lane == 0) a.heads[(size_t)t * a.h + r] = bj;
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      if (lane + 64 * u == bj) avail[u] = false;
+    if (rank < a.h) a.heads[(size_t)t * a.h + rank] = tid;
   }
 }
 
@@ -184,7 +243,7 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
   else launch_partial<8>(a, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(route_final_kernel, dim3(a.T), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(route_final_kernel, dim3(a.T), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

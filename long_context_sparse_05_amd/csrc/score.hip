@@ -10,26 +10,31 @@
 // The head-token products are a dense contraction over d = 128, so they run
 // on v_mfma_f32_16x16x32_bf16: A = the query's (gathered) head rows, padded to
 // 16-row tiles and held in registers for the whole workgroup; B = 16 keys per
-// MFMA column tile, loaded straight from HBM into registers (each lane loads
-// 16 contiguous bytes of one key, so a wave reads 16 whole 256-byte keys in
-// four instructions).  Keys are read exactly once.  The weighted ReLU and the
-// head reduction run on the accumulators in registers (four rows per lane,
-// then two cross-lane adds).  The epilogue also builds a 4096-bin histogram
-// of the top 12 bits of each score's order key, the first radix digit of the
-// per-row top-k, so the selection needs no extra pass over the scores.
+// MFMA column tile.  Keys are streamed from HBM exactly once with coalesced
+// non-temporal 16-byte loads (a wave instruction covers four whole 256-byte
+// keys, 1 KiB contiguous), then passed through a per-wave LDS tile whose rows
+// are padded to 272 bytes, so the MFMA-layout reads (lane = key column,
+// lane group = 8-element slice of d) hit 16 distinct bank groups.  The
+// weighted ReLU and the head reduction run on the accumulators in registers
+// (four rows per lane, then two cross-lane adds).  The epilogue also builds a
+// 4096-bin histogram of the top 12 bits of each score's order key, the first
+// radix digit of the per-row top-k.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace misa {
 
+constexpr int kKeyRowLds = 272;  // bytes per key row in the LDS tile (256 + 16)
+
 template <int HT, bool GATHER, int U>
 __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
   __shared__ uint32_t lds_hist[kHistBins];
+  __shared__ uint4 tile[4][16 * kKeyRowLds / 16];
   const int t = blockIdx.y;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
-  const int col = lane & 15;   // MFMA column (key) within a 16-key tile
-  const int grp = lane >> 4;   // lane group: k sub-slice / accumulator rows
+  const int col = lane & 15;   // MFMA column (key) / 16-byte slice of a key row
+  const int grp = lane >> 4;   // lane group: k sub-slice / accumulator rows / key of a load
   const bool hist = a.hist != nullptr;
 
   const int c0 = blockIdx.x * a.chunk;
@@ -42,9 +47,9 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
   if (hist) {
     for (int b = threadIdx.x; b < kHistBins; b += 256) lds_hist[b] = 0;
   }
-  if (!GATHER && c0 >= nvalid) {
+  if (!GATHER && c0 >= nvalid) {  // uniform across the workgroup: no barrier follows
     for (int c = c0 + threadIdx.x; c < c1; c += 256) srow[c] = -INFINITY;
-    return;  // uniform across the workgroup: no barrier follows for it
+    return;
   }
 
   // Query head fragments (A operand) and the weights of this lane's rows.
@@ -77,28 +82,36 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
   if (hist) __syncthreads();
 
   const int32_t *crow = GATHER ? a.cand + (size_t)t * a.ncols : nullptr;
-  for (int base = c0 + wave * 16 * U; base < c1; base += 4 * 16 * U) {
-    uint4 kv[U][4];
-    bool ok[U];
+  char *wt = (char *)tile[wave];
+  // U tiles of 16 keys per step; load i of tile u covers keys 4i..4i+3
+  auto load_step = [&](int base, uint4 (&kv)[U][4]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int c = base + u * 16 + col;
-      int tok = -1;
-      if (c < c1 && c < nvalid) tok = GATHER ? crow[c] : c;
-      ok[u] = tok >= 0;
-      const uint16_t *kp = a.keys + (seq_base + (size_t)(tok >= 0 ? tok : 0)) * kD + grp * 8;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        kv[u][s] = ok[u] ? *(const uint4 *)(kp + s * 32) : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const int c = base + u * 16 + 4 * i + grp;
+        int tok = -1;
+        if (c < c1 && c < nvalid) tok = GATHER ? crow[c] : c;
+        kv[u][i] = tok >= 0 ? load_nt16(a.keys + (seq_base + (size_t)tok) * kD + col * 8)
+                            : make_uint4(0, 0, 0, 0);
+      }
     }
+  };
+  auto process_step = [&](int base, const uint4 (&kv)[U][4]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      // transpose through LDS: row = key within the tile, 16-byte slices
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *(uint4 *)(wt + (4 * i + grp) * kKeyRowLds + col * 16) = kv[u][i];
+      uint4 kb[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) kb[s] = *(const uint4 *)(wt + col * kKeyRowLds + (4 * s + grp) * 16);
       float part = 0.f;
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma16(qa[ht][s], as_bf16x8(kv[u][s]), acc);
+        for (int s = 0; s < 4; ++s) acc = mfma16(qa[ht][s], as_bf16x8(kb[s]), acc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) part += wv[ht][r] * fmaxf(acc[r], 0.f);
       }
@@ -106,11 +119,25 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
       part += __shfl_xor(part, 32, kWave);
       const int c = base + u * 16 + col;
       if (grp == 0 && c < c1) {
-        const float sc = ok[u] ? part : -INFINITY;
+        const bool ok = c < nvalid && (!GATHER || crow[c] >= 0);
+        const float sc = ok ? part : -INFINITY;
         srow[c] = sc;
-        if (hist && ok[u]) atomicAdd(&lds_hist[order_key(sc) >> kHistShift], 1u);
+        if (hist && ok) atomicAdd(&lds_hist[order_key(sc) >> kHistShift], 1u);
       }
     }
+  };
+  // software pipeline over two register buffers: the next step's loads are
+  // in flight while the current step is transposed, contracted and stored
+  const int stride = 4 * 16 * U;
+  uint4 ka[U][4], kb2[U][4];
+  int base = c0 + wave * 16 * U;
+  if (base < c1) load_step(base, ka);
+  for (; base < c1; base += 2 * stride) {
+    if (base + stride < c1) load_step(base + stride, kb2);
+    process_step(base, ka);
+    if (base + stride >= c1) break;
+    if (base + 2 * stride < c1) load_step(base + 2 * stride, ka);
+    process_step(base + stride, kb2);
   }
   if (hist) {
     __syncthreads();
@@ -125,7 +152,7 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
 template <int HT, bool GATHER>
 static hipError_t launch_ht(const ScoreArgs &a, hipStream_t st) {
   dim3 grid((a.ncols + a.chunk - 1) / a.chunk, a.T);
-  hipLaunchKernelGGL((score_rows_kernel<HT, GATHER, 4>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((score_rows_kernel<HT, GATHER, 2>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -7,100 +7,50 @@
 // key (order_key(score) << 32) | ~token: keys are unique and their order is
 // exactly the ranking, so the top-k is "every key >= the k-th largest key".
 //
-//  1. histogram of the top 12 bits (fused into the scoring epilogue, or
-//     topk_hist_kernel for caller-provided scores);
-//  2. topk_filter_kernel (many workgroups per row): every workgroup finds the
-//     digit b1 holding the k-th key from the 4096-bin histogram; columns
-//     above b1 are written straight to the output (wave-aggregated atomics),
-//     columns equal to b1 are appended to a per-row candidate list;
-//  3. topk_finish_kernel (one workgroup per row): the candidates are loaded
-//     into LDS (up to 16384 of them; beyond that they are re-read from the
-//     score row) and the remaining 52 key bits are resolved with 8-bit digit
-//     passes over LDS histograms, emitting every key above each pass's
-//     crossing digit, until the crossing bin holds exactly what is needed.
+//  1. a 4096-bin histogram of the top 12 key bits, accumulated into the
+//     workspace by the scoring kernel's epilogue (or topk_hist_kernel for
+//     caller-provided scores);
+//  2. topk_filter_kernel, many workgroups per row: the digit b1 holding the
+//     kk-th key comes from the histogram; columns above b1 go straight to
+//     the output and columns equal to b1 (the candidates) to a per-row list.
+//     Positions within a workgroup come from a block-wide scan, and ONE
+//     global atomic per counter per 4096 columns reserves the workgroup's
+//     range (same-address global atomics serialise: per-element or per-wave
+//     atomics from hundreds of workgroups would dominate);
+//  3. topk_finish_kernel, one 1024-thread workgroup per row: the candidates
+//     are loaded into LDS and the remaining 52 key bits resolved with 8-bit
+//     digit passes over LDS histograms, emitting every key above each pass's
+//     crossing digit and compacting the survivors, until the crossing bin
+//     holds exactly the keys still needed.  More than 16384 candidates
+//     (heavy ties) are re-read from the score row instead.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace misa {
 
-constexpr int kFinishCap = 16384;  // candidates resolved in LDS (128 KiB)
-
-struct Thresh {
-  int b1;          // first digit holding the kk-th key
-  uint32_t above;  // keys with first digit > b1
-  uint32_t eq;     // keys with first digit == b1
-  uint32_t kk;     // min(k, number of valid columns)
-};
-
-__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
-// Block-wide inclusive scan of one value per thread (256 threads, 4 waves).
-__device__ __forceinline__ uint32_t block_scan256(uint32_t v, uint32_t *sh4, uint32_t &total) {
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t y = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += y;
-  }
-  if (lane == kWave - 1) sh4[wave] = incl;
-  __syncthreads();
-  uint32_t base = 0;
-  total = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t x = sh4[i];
-    if (i < wave) base += x;
-    total += x;
-  }
-  __syncthreads();
-  return base + incl;
-}
-
-// Threshold digit of one row from its 4096-bin histogram (256 threads).
-// Thread tid owns 16 consecutive bins, counted from the top.
-__device__ Thresh row_threshold(const uint32_t *hrow, uint32_t k, uint32_t *sh) {
-  const int tid = threadIdx.x;
-  const int top = kHistBins - 1 - 16 * tid;
-  uint32_t v[16];
-  uint32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    v[i] = hrow[top - i];
-    s += v[i];
-  }
-  uint32_t total;
-  const uint32_t incl = block_scan256(s, sh, total);
-  const uint32_t excl = incl - s;
-  const uint32_t kk = min(k, total);
-  if (kk > 0 && excl < kk && kk <= incl) {
-    uint32_t cum = excl;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (cum + v[i] >= kk) {
-        sh[4] = (uint32_t)(top - i);
-        sh[5] = cum;
-        sh[6] = v[i];
-        break;
-      }
-      cum += v[i];
-    }
-  }
-  __syncthreads();
-  Thresh th;
-  th.kk = kk;
-  th.b1 = kk ? (int)sh[4] : kHistBins;
-  th.above = kk ? sh[5] : 0;
-  th.eq = kk ? sh[6] : 0;
-  __syncthreads();
-  return th;
-}
+constexpr int kSelThreads = 1024;
+constexpr int kSelCap = 16384;      // candidates resolved in LDS (128 KiB)
+constexpr int kSelCompact = 2048;   // survivors compacted after each pass
 
 __device__ __forceinline__ int row_valid_len(const TopkArgs &a, int r) {
   return a.row_len ? max(0, min(a.ld, a.row_len[r] + a.row_len_add)) : a.ld;
+}
+
+// Wave-aggregated append to an LDS counter: one atomic per wave.
+__device__ __forceinline__ bool lds_append(bool pred, uint32_t *counter, uint32_t &pos) {
+  const uint64_t m = __ballot(pred);
+  if (!m) return false;
+  const int leader = __ffsll((unsigned long long)m) - 1;
+  uint32_t base = 0;
+  if (lane_id() == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
+  base = __shfl(base, leader, kWave);
+  pos = base + lanes_below(m);
+  return pred;
+}
+
+__device__ __forceinline__ uint64_t composite(uint32_t key, int tok) {
+  return ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)tok);
 }
 
 // ---------------------------------------------------------------- histogram
@@ -122,114 +72,176 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(TopkArgs a, uint32_t *hi
 }
 
 // ------------------------------------------------------------------- filter
+// Positions come from one block-wide scan per round of 4096 columns, and the
+// results go to this workgroup's own slots: no atomics and no staging
+// buffers, so several workgroups fit on a CU.
 template <bool MAP>
 __global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a) {
-  __shared__ uint32_t sh[8];
+  constexpr int kSub = 4096;  // columns per round: 16 per thread
+  __shared__ uint32_t lh[kHistBins];
+  __shared__ uint32_t sh[16];
   const int r = blockIdx.y;
-  const Thresh th = row_threshold(a.hist + (size_t)r * kHistBins, (uint32_t)a.k, sh);
-  if (th.kk == 0) return;
+  const int tid = threadIdx.x;
   const int n = row_valid_len(a, r);
   const int c0 = blockIdx.x * a.chunk, c1 = min(c0 + a.chunk, n);
-  const bool keep = th.eq <= (uint32_t)a.cap;
-  const int lane = lane_id();
-  uint32_t *cnt = a.counters + (size_t)r * 4;
   const float *srow = a.scores + (size_t)r * a.ld;
+  const int32_t *mrow = MAP ? a.map + (size_t)r * a.ld : nullptr;
+  const bool vec = (a.ld % 4) == 0;  // 16-byte aligned rows
+
+  auto load_round = [&](int sb, float (&sv)[4][4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int cf = sb + u * 1024 + 4 * tid;
+      if (vec && cf + 3 < c1) {
+        const float4 x = *(const float4 *)(srow + cf);
+        sv[u][0] = x.x; sv[u][1] = x.y; sv[u][2] = x.z; sv[u][3] = x.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[u][e] = cf + e < c1 ? srow[cf + e] : 0.f;
+      }
+    }
+  };
+  // the first round's scores are requested before the threshold is known
+  float sv[4][4];
+  load_round(c0, sv);
+  {
+    const uint4 *h4 = (const uint4 *)(a.hist + (size_t)r * kHistBins);
+#pragma unroll
+    for (int i = 0; i < kHistBins / 4 / 256; ++i) ((uint4 *)lh)[tid + 256 * i] = h4[tid + 256 * i];
+  }
+  __syncthreads();
+  const Thresh th = threshold_from_lds<256>(lh, (uint32_t)a.k, sh);
+  if (blockIdx.x == 0 && tid == 0) {
+    uint32_t *cnt = a.counters + (size_t)r * kRowCounters;
+    cnt[4] = (uint32_t)th.b1;
+    cnt[5] = th.above;
+    cnt[6] = th.eq;
+    cnt[7] = th.kk;
+  }
+  if (th.kk == 0) return;  // uniform; the finish reads nothing else then
+  const bool keep = th.eq <= (uint32_t)a.cap;
+  uint32_t *cnt = a.counters + (size_t)r * kRowCounters;
   int32_t *irow = a.idx + (size_t)r * a.k;
   float *vrow = a.val ? a.val + (size_t)r * a.k : nullptr;
   uint2 *crow = a.cand + (size_t)r * a.cap;
-  for (int cb = c0; cb < c1; cb += 256) {  // same trip count for every lane
-    const int c = cb + threadIdx.x;
-    bool valid = c < c1;
-    int tok = c;
-    if (MAP && valid) {
-      tok = a.map[(size_t)r * a.ld + c];
-      valid = tok >= 0;
+  for (int sb = c0; sb < c1; sb += kSub) {  // uniform trip count
+    if (sb != c0) load_round(sb, sv);
+    uint32_t fs = 0, fc = 0;  // this thread's 16 columns: above b1 / equal to b1
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = sb + u * 1024 + 4 * tid + e;
+        bool valid = c < c1;
+        if (MAP && valid) valid = mrow[c] >= 0;
+        const int dg = (int)(order_key(sv[u][e]) >> kHistShift);
+        fs |= (valid && dg > th.b1 ? 1u : 0u) << (u * 4 + e);
+        fc |= (valid && keep && dg == th.b1 ? 1u : 0u) << (u * 4 + e);
+      }
     }
-    const float s = valid ? srow[c] : 0.f;
-    const uint32_t key = order_key(s);
-    const int dg = (int)(key >> kHistShift);
-    const bool sel = valid && dg > th.b1;
-    const bool cnd = valid && keep && dg == th.b1;
-    const uint64_t ms = __ballot(sel);
-    if (ms) {
-      const int leader = __ffsll((unsigned long long)ms) - 1;
-      uint32_t base = 0;
-      if (lane == leader) base = atomicAdd(&cnt[0], (uint32_t)__popcll(ms));
-      base = __shfl(base, leader, kWave);
-      if (sel) {
-        const uint32_t pos = base + lanes_below(ms);
-        if (pos < th.above) {
-          irow[pos] = tok;
-          if (vrow) vrow[pos] = s;
+    const uint32_t mine = ((uint32_t)__popc(fs) << 16) | (uint32_t)__popc(fc);
+    uint32_t total;
+    const uint32_t excl = block_scan<256>(mine, sh, total) - mine;
+    // one global atomic per counter per round reserves this workgroup's range
+    if (tid == 0) {
+      sh[8] = (total >> 16) ? atomicAdd(&cnt[0], total >> 16) : 0u;
+      sh[9] = (total & 0xFFFFu) ? atomicAdd(&cnt[1], total & 0xFFFFu) : 0u;
+    }
+    __syncthreads();
+    uint32_t so = sh[8] + (excl >> 16), co = sh[9] + (excl & 0xFFFFu);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int bit = u * 4 + e;
+        const int c = sb + u * 1024 + 4 * tid + e;
+        if ((fs >> bit) & 1u) {
+          if (so < th.above) {
+            irow[so] = MAP ? mrow[c] : c;
+            if (vrow) vrow[so] = sv[u][e];
+          }
+          ++so;
+        }
+        if ((fc >> bit) & 1u) {
+          if (co < (uint32_t)a.cap) crow[co] = make_uint2(order_key(sv[u][e]), (uint32_t)c);
+          ++co;
         }
       }
     }
-    const uint64_t mc = __ballot(cnd);
-    if (mc) {
-      const int leader = __ffsll((unsigned long long)mc) - 1;
-      uint32_t base = 0;
-      if (lane == leader) base = atomicAdd(&cnt[1], (uint32_t)__popcll(mc));
-      base = __shfl(base, leader, kWave);
-      if (cnd) {
-        const uint32_t pos = base + lanes_below(mc);
-        if (pos < (uint32_t)a.cap) crow[pos] = make_uint2(key, (uint32_t)c);
-      }
-    }
+    __syncthreads();  // sh[8..9] are rewritten next round
   }
 }
 
 // ------------------------------------------------------------------- finish
 template <bool MAP>
-__global__ __launch_bounds__(256) void topk_finish_kernel(TopkArgs a) {
-  __shared__ uint64_t cs[kFinishCap];
+__global__ __launch_bounds__(kSelThreads) void topk_finish_kernel(TopkArgs a) {
+  constexpr int NT = kSelThreads;
+  constexpr int NW = NT / kWave;
+  __shared__ uint64_t cs[kSelCap];
+  __shared__ uint64_t cs2[kSelCompact];
   __shared__ uint32_t hs[256];
-  __shared__ uint32_t sh[16];
+  __shared__ uint32_t sh[NW + 16];  // [0, NW) scan scratch, then counters and pass results
+  uint32_t *ctr = sh + NW;          // [0] next output slot [1] compacted
+  uint32_t *res = sh + NW + 4;      // [0] digit [1] count above it [2] count in it
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
-  const Thresh th = row_threshold(a.hist + (size_t)r * kHistBins, (uint32_t)a.k, sh);
+  const uint32_t *cnt = a.counters + (size_t)r * kRowCounters;
+  Thresh th;
+  th.b1 = (int)cnt[4];
+  th.above = cnt[5];
+  th.eq = cnt[6];
+  th.kk = cnt[7];
+
   int32_t *irow = a.idx + (size_t)r * a.k;
   float *vrow = a.val ? a.val + (size_t)r * a.k : nullptr;
-  for (int i = (int)th.kk + tid; i < a.k; i += 256) {
+  for (int i = (int)th.kk + tid; i < a.k; i += NT) {
     irow[i] = -1;
     if (vrow) vrow[i] = -INFINITY;
   }
-  if (th.kk == 0) return;
+  if (th.kk == 0) return;  // uniform
 
-  const bool in_lds = th.eq <= (uint32_t)a.cap;
-  const int ncand = in_lds ? (int)th.eq : 0;
   const int n = row_valid_len(a, r);
   const float *srow = a.scores + (size_t)r * a.ld;
   const int32_t *mrow = MAP ? a.map + (size_t)r * a.ld : nullptr;
-  if (in_lds) {
+  const bool keep = th.eq <= (uint32_t)a.cap;
+  uint64_t *cur = cs;
+  int ncur = keep ? (int)min(th.eq, (uint32_t)a.cap) : 0;
+  if (keep) {
     const uint2 *crow = a.cand + (size_t)r * a.cap;
-    for (int i = tid; i < ncand; i += 256) {
+    for (int i = tid; i < ncur; i += NT) {
       const uint2 e = crow[i];
-      const int tok = MAP ? mrow[e.y] : (int)e.y;
-      cs[i] = ((uint64_t)e.x << 32) | (uint32_t)(~(uint32_t)tok);
+      cs[i] = composite(e.x, MAP ? mrow[e.y] : (int)e.y);
     }
   }
-  if (tid == 0) sh[8] = th.above;  // next output slot
+  if (tid == 0) ctr[0] = th.above;
   __syncthreads();
 
-  // Visit every candidate composite key: from LDS, or (too many candidates)
-  // straight from the score row.
-  auto for_each = [&](auto &&fn) {
-    if (in_lds) {
-      for (int i = tid; i < ncand; i += 256) fn(cs[i]);
-    } else {
-      for (int c = tid; c < n; c += 256) {
-        int tok = c;
-        if (MAP) {
-          tok = mrow[c];
-          if (tok < 0) continue;
+  // Visit every candidate that matches (prefix, mask) in uniform rounds of NT
+  // (wave ballots stay legal): from LDS, or (too many ties) from the row.
+  auto for_each = [&](uint64_t prefix, uint64_t mask, auto &&fn) {
+    const int total = keep ? ncur : n;
+    for (int b = 0; b < total; b += NT) {
+      const int i = b + tid;
+      bool ok = i < total;
+      uint64_t ck = 0;
+      if (ok) {
+        if (keep) {
+          ck = cur[i];
+        } else {
+          int tok = i;
+          if (MAP) {
+            tok = mrow[i];
+            ok = tok >= 0;
+          }
+          if (ok) ck = composite(order_key(srow[i]), tok);
         }
-        fn(((uint64_t)order_key(srow[c]) << 32) | (uint32_t)(~(uint32_t)tok));
       }
+      fn(ok && (ck & mask) == prefix, ck);
     }
   };
-  auto emit = [&](uint64_t ck) {
-    const uint32_t pos = atomicAdd(&sh[8], 1u);
-    if (pos < th.kk) {
+  auto emit = [&](bool pred, uint64_t ck) {
+    uint32_t pos;
+    if (lds_append(pred, &ctr[0], pos) && pos < th.kk) {
       irow[pos] = (int32_t)(~(uint32_t)ck);
       if (vrow) vrow[pos] = key_to_float((uint32_t)(ck >> 32));
     }
@@ -240,34 +252,45 @@ __global__ __launch_bounds__(256) void topk_finish_kernel(TopkArgs a) {
   uint64_t mask = 0xFFFull << 52;
   for (int pass = 0; pass < 7; ++pass) {
     const int shift = pass < 6 ? 44 - 8 * pass : 0;
-    hs[tid] = 0;
+    if (tid < 256) hs[tid] = 0;
     __syncthreads();
-    for_each([&](uint64_t ck) {
-      if ((ck & mask) == prefix) atomicAdd(&hs[(uint32_t)(ck >> shift) & 0xFFu], 1u);
+    for_each(prefix, mask, [&](bool ok, uint64_t ck) {
+      if (ok) atomicAdd(&hs[(uint32_t)(ck >> shift) & 0xFFu], 1u);
     });
     __syncthreads();
-    const uint32_t v = hs[255 - tid];  // thread 0 holds the largest digit
+    const uint32_t v = tid < 256 ? hs[255 - tid] : 0u;  // thread 0: the largest digit
     uint32_t total;
-    const uint32_t incl = block_scan256(v, sh, total);
+    const uint32_t incl = block_scan<NT>(v, sh, total);
     const uint32_t excl = incl - v;
-    if (excl < need && need <= incl) {
-      sh[4] = 255 - tid;
-      sh[5] = excl;
-      sh[6] = v;
+    if (tid < 256 && excl < need && need <= incl) {
+      res[0] = 255 - tid;
+      res[1] = excl;
+      res[2] = v;
     }
     __syncthreads();
-    const uint32_t d = sh[4], above_d = sh[5], cnt_d = sh[6];
-    for_each([&](uint64_t ck) {
-      if ((ck & mask) == prefix && ((uint32_t)(ck >> shift) & 0xFFu) > d) emit(ck);
+    const uint32_t d = res[0], above_d = res[1], cnt_d = res[2];
+    for_each(prefix, mask, [&](bool ok, uint64_t ck) {
+      emit(ok && ((uint32_t)(ck >> shift) & 0xFFu) > d, ck);
     });
     need -= above_d;
     prefix |= (uint64_t)d << shift;
     mask |= 0xFFull << shift;
     if (cnt_d == need || pass == 6) {
-      for_each([&](uint64_t ck) {
-        if ((ck & mask) == prefix) emit(ck);
-      });
+      for_each(prefix, mask, [&](bool ok, uint64_t ck) { emit(ok, ck); });
       break;
+    }
+    if (keep && cnt_d <= (uint32_t)kSelCompact) {  // keep only the survivors
+      uint64_t *dst = (cur == cs) ? cs2 : cs;
+      if (tid == 0) ctr[1] = 0;
+      __syncthreads();
+      for_each(prefix, mask, [&](bool ok, uint64_t ck) {
+        uint32_t pos;
+        if (lds_append(ok, &ctr[1], pos) && pos < (uint32_t)(dst == cs2 ? kSelCompact : kSelCap))
+          dst[pos] = ck;
+      });
+      __syncthreads();
+      cur = dst;
+      ncur = (int)cnt_d;
     }
     __syncthreads();
   }
@@ -294,21 +317,19 @@ hipError_t launch_topk_hist(const TopkArgs &a, uint32_t *hist, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_topk_filter(const TopkArgs &a, hipStream_t st) {
+hipError_t launch_topk_select(const TopkArgs &a, hipStream_t st) {
+  if (a.cap > kSelCap) return hipErrorInvalidValue;
   dim3 grid((a.ld + a.chunk - 1) / a.chunk, a.rows);
   if (a.map)
     hipLaunchKernelGGL(topk_filter_kernel<true>, grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL(topk_filter_kernel<false>, grid, dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_topk_finish(const TopkArgs &a, hipStream_t st) {
-  if (a.cap > kFinishCap) return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (a.map)
-    hipLaunchKernelGGL(topk_finish_kernel<true>, dim3(a.rows), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(topk_finish_kernel<true>, dim3(a.rows), dim3(kSelThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(topk_finish_kernel<false>, dim3(a.rows), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(topk_finish_kernel<false>, dim3(a.rows), dim3(kSelThreads), 0, st, a);
   return hipGetLastError();
 }
 

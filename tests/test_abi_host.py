@@ -63,7 +63,7 @@ def test_workspace_sizes(lib):
     b = batch()
     for op, kw in ((abi.MISA_OP_ROUTE, dict(B=64, h=8)), (abi.MISA_OP_SCORE_TOPK, dict(k=256)),
                    (abi.MISA_OP_DENSE, dict(k=256)), (abi.MISA_OP_RERANK, dict(k=256, kc=1024)),
-                   (abi.MISA_OP_TOPK, dict(k=256))):
+                   (abi.MISA_OP_TOPK, dict(k=256)), (abi.MISA_OP_INDEXER, dict(B=64, h=8, k=256))):
         rc, n = ws_bytes(lib, b, op, **kw)
         assert rc == OK and n > 0 and n % 256 == 0
     # the score workspace holds at least the fp32 score rows
@@ -118,3 +118,8 @@ def test_validation_before_any_hip_call(lib):
     assert lib.indexer_dense(ctypes.byref(b), 64, F, None, F, small, None) == ERR_WORKSPACE
     assert lib.misa_rerank(ctypes.byref(b), F, 128, 64, F, None, F, small, None) == ERR_WORKSPACE
     assert lib.misa_topk(F, 4, 64, F, 8, F, None, F, small, None) == ERR_WORKSPACE
+    assert lib.misa_indexer(ctypes.byref(b), F, 64, 8, 0, 64, F, None, F, None, F, small, None) == ERR_WORKSPACE
+    assert lib.misa_indexer(ctypes.byref(b), None, 64, 8, 0, 64, F, None, F, None, F, big, None) == ERR_NULL
+    assert lib.misa_indexer(ctypes.byref(b), F, 64, 9999, 0, 64, F, None, F, None, F, big, None) == ERR_SHAPE
+    assert lib.misa_indexer(ctypes.byref(b), F, 64, 8, 3, 64, F, None, F, None, F, big, None) == ERR_SHAPE
+    assert lib.misa_indexer(ctypes.byref(b), F, 64, 8, 0, 0, F, None, F, None, F, big, None) == ERR_SHAPE

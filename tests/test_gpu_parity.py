@@ -296,3 +296,34 @@ def test_gpu_invariants(seed):
     cand, _ = abi.score_topk(b, heads, 3000)
     fin, _ = abi.rerank(b, cand, k)
     assert [set(r) for r in np_(dense)] == [set(r) for r in np_(fin)]
+
+
+# ------------------------------------------------------------ fused indexer
+@pytest.mark.parametrize("S,Lmax,T,H,seed", CASES[:4])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_indexer_fused_equals_separate_calls(S, Lmax, T, H, seed, mode):
+    """misa_indexer = misa_route then misa_score_topk, bit for bit; its
+    selection also passes the oracle comparison."""
+    abi = _abi()
+    case = make(S, Lmax, T, H, seed)
+    b = upload(case)
+    B, h, k = 64, min(8, H), min(300, Lmax)
+    pooled = abi.pool(b, B)
+    heads_sep = abi.route(b, pooled, B, h, mode)
+    idx_sep, val_sep = abi.score_topk(b, heads_sep, k)
+    for rep in range(2):  # the workspace holds the previous call's contents the second time
+        ws = b.workspace(abi.MISA_OP_INDEXER, B=B, h=h, k=k)
+        heads, idx, val = abi.indexer(b, pooled, B, h, k, mode=mode, ws=ws)
+        assert np.array_equal(np_(heads), np_(heads_sep))
+        gi, gv = np_(idx), np_(val)
+        si, sv = np_(idx_sep), np_(val_sep)
+        for t in range(T):
+            assert set(gi[t]) == set(si[t])
+            assert np.array_equal(np.sort(gv[t]), np.sort(sv[t]))
+    ob = orc.Batch.from_case(case)
+    om = orc.misa(ob, B, h, k, mode=mode, want_scores=True)
+    for t in range(T):
+        n = int(n_valid(case)[t])
+        if sorted(gi[t]) != sorted(om["idx"][t]):
+            parity.check_set(gi[t], om["idx"][t], lambda i: om["scores"][t, i], n, k,
+                             parity.row_sbar(om["scores"][t], n))
