@@ -27,7 +27,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 KEY_BYTES = 128 * 2  # one bf16 indexing key
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "long_context_sparse_05_amd", "csrc", f)
-                  for f in ("score.hip", "common.hpp", "kernels.hpp")]
+                  for f in ("score.hip", "common.hpp")]
 
 
 class HipEvents:
@@ -77,22 +77,96 @@ def traffic_for(workload):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(case, cfg, reps=3):
-    """The oracle (fp64 C, OpenMP) on the whole workload: router, routed
-    scoring and top-k per query.  Returns (value, cores, sample, outputs)."""
+COPY_MIB = 512
+
+
+def copy_calibration():
+    """A plain device copy of known size (COPY_MIB MiB read, COPY_MIB MiB
+    written), run under rocprofv3 --pmc to scale FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    src = torch.empty(COPY_MIB << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_MIB << 20, "launches": 3}), flush=True)
+    return 0
+
+
+def _counter_rows(path):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    rows = []
+    for f in files:
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def _per_kernel_kib(rows, counter, name_part):
+    """Mean counter value per dispatch of the kernels whose name contains
+    name_part."""
+    vals = [float(r["Counter_Value"]) for r in rows
+            if r.get("Counter_Name") == counter and name_part in r.get("Kernel_Name", "")]
+    return sum(vals) / len(vals) if vals else None
+
+
+def summarize_counters(workload, fetch_dir, write_dir, cfetch_dir, cwrite_dir):
+    """Write the scoring kernel's HBM traffic per launch (FETCH_SIZE and
+    WRITE_SIZE, each scaled by the same counter on the plain copy of known
+    size) to profiles/score_kernel_traffic.json, keyed by the kernel-source
+    hash so a changed kernel reads as unmeasured."""
+    kname = "score_rows_kernel"
+    f_k = _per_kernel_kib(_counter_rows(fetch_dir), "FETCH_SIZE", kname)
+    w_k = _per_kernel_kib(_counter_rows(write_dir), "WRITE_SIZE", kname)
+    # the runtime's device copy kernel moves the known bytes (torch's fill of
+    # the source buffer is a separate, small dispatch)
+    f_c = _per_kernel_kib(_counter_rows(cfetch_dir), "FETCH_SIZE", "copyBuffer")
+    w_c = _per_kernel_kib(_counter_rows(cwrite_dir), "WRITE_SIZE", "copyBuffer")
+    copy_kib = (COPY_MIB << 20) / 1024.0
+    fs = copy_kib / f_c if f_c else None
+    wsf = copy_kib / w_c if w_c else None
+    rec = {}
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+    ent = {"kernel_hash": kernel_hash(), "fetch_kib_raw": f_k, "write_kib_raw": w_k,
+           "copy_fetch_kib_raw": f_c, "copy_write_kib_raw": w_c,
+           "fetch_scale": fs, "write_scale": wsf}
+    if f_k is not None and w_k is not None and fs and wsf:
+        ent["bytes_per_launch"] = (f_k * fs + w_k * wsf) * 1024.0
+    rec[workload] = ent
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1)
+    print(json.dumps(ent), flush=True)
+    return 0
+
+
+def cpu_baseline_rows(case, cfg, rows, reps=3):
+    """The oracle on the query rows `rows` of the workload (all rows unless the
+    workload is too large for the host in ~30 s).  Returns (value, cores,
+    outputs)."""
     import numpy as np
     from oracle import oracle as orc
-    b = orc.Batch.from_case(case)
+    sub = dict(case)
+    for key in ("q", "w", "q_seq", "q_pos"):
+        sub[key] = np.ascontiguousarray(case[key][rows])
+    b = orc.Batch.from_case(sub)
+    kind = cfg["kind"]
     times = []
     out = None
     for _ in range(reps):
         t0 = time.perf_counter()
-        out = orc.misa(b, cfg["B"], cfg["h"], cfg["k"])
+        if kind == "dagger":
+            out = orc.misa_dagger(b, cfg["B"], cfg["h"], cfg["kc"], cfg["k"])
+        elif "h" in cfg:
+            out = orc.misa(b, cfg["B"], cfg["h"], cfg["k"])
+        else:
+            idx, _ = orc.dsa(b, cfg["k"])
+            out = {"idx": idx}
         times.append(time.perf_counter() - t0)
-    dt = float(np.median(times))
-    n = float((case["q_pos"].astype(np.int64) + 1).sum())
-    return n / dt, orc.num_threads(), "all %d queries of the workload, median of %d runs" % (
-        case["q_pos"].size, reps), out
+    n = float((sub["q_pos"].astype(np.int64) + 1).sum())
+    return n / float(np.median(times)), orc.num_threads(), out
 
 
 def main(argv=None):
@@ -102,7 +176,15 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="misa_decode_16x128K")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain copy of known size (for counter scaling)")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"),
+                    help="rocprofv3 --pmc output dirs of the bench and of --copy-calibration")
     args = ap.parse_args(argv)
+    if args.summarize_counters:
+        return summarize_counters(args.workload, *args.summarize_counters)
+    if args.copy_calibration:
+        return copy_calibration()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the indexer path here is built and timed on a single "
               "MI355X; --gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -117,40 +199,55 @@ def main(argv=None):
         return 1
     abi.load()
     case, cfg = synth.make_workload(args.workload, seed=0)
-    if cfg["kind"] != "decode" or "h" not in cfg:
-        print("bench.py times the MISA decode step; workload %s is a parity case" % args.workload,
-              file=sys.stderr)
-        return 2
-    B, h, k = cfg["B"], cfg["h"], cfg["k"]
+    kind = cfg["kind"]
+    routed = "h" in cfg
+    B, h, k = cfg.get("B"), cfg.get("h"), cfg["k"]
+    kc = cfg.get("kc", k)
     b = abi.Batch.from_numpy(case)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     ev = HipEvents()
-
-    # once per key cache: block pooling
-    pooled = abi.pool(b, B)
-    e0, e1 = ev.create(), ev.create()
-    ev.record(e0, sp)
-    for _ in range(3):
-        abi.pool(b, B, out=pooled)
-    ev.record(e1, sp)
-    pool_us = ev.ms(e0, e1) / 3 * 1e3
-
-    heads = torch.empty((b.T, h), dtype=torch.int32, device="cuda")
-    idx = torch.empty((b.T, k), dtype=torch.int32, device="cuda")
-    val = torch.empty((b.T, k), dtype=torch.float32, device="cuda")
-    ws_r = b.workspace(abi.MISA_OP_ROUTE, B=B, h=h)
-    ws_s = b.workspace(abi.MISA_OP_SCORE_TOPK, h=h, k=k)
-    ws_i = b.workspace(abi.MISA_OP_INDEXER, B=B, h=h, k=k)
     K = args.steps
-    sev = [(ev.create(), ev.create()) for _ in range(K)]
+    dev = "cuda"
 
-    def step(events=None):  # the fused call: router, routed scoring, top-k
-        abi.indexer(b, pooled, B, h, k, heads=heads, idx=idx, val=val, ws=ws_i, events=events)
+    pool_us = None
+    pooled = None
+    if routed:  # once per key cache: block pooling
+        pooled = abi.pool(b, B)
+        e0, e1 = ev.create(), ev.create()
+        ev.record(e0, sp)
+        for _ in range(3):
+            abi.pool(b, B, out=pooled)
+        ev.record(e1, sp)
+        pool_us = ev.ms(e0, e1) / 3 * 1e3
 
-    def step_separate():  # the same step as two calls
+    k1 = kc if kind == "dagger" else k  # selection size of the scoring call
+    heads = torch.empty((b.T, h), dtype=torch.int32, device=dev) if routed else None
+    idx = torch.empty((b.T, k1), dtype=torch.int32, device=dev)
+    val = torch.empty((b.T, k1), dtype=torch.float32, device=dev)
+    fin = torch.empty((b.T, k), dtype=torch.int32, device=dev)
+    fin_val = torch.empty((b.T, k), dtype=torch.float32, device=dev)
+    if routed:
+        ws_i = b.workspace(abi.MISA_OP_INDEXER, B=B, h=h, k=k1)
+        ws_r = b.workspace(abi.MISA_OP_ROUTE, B=B, h=h)
+        ws_s = b.workspace(abi.MISA_OP_SCORE_TOPK, h=h, k=k1)
+    else:
+        ws_d = b.workspace(abi.MISA_OP_DENSE, k=k)
+    ws_rr = b.workspace(abi.MISA_OP_RERANK, k=k, kc=kc) if kind == "dagger" else None
+
+    def step(events=None):
+        if routed:  # the fused call: router, routed scoring, top-k (k' for MISA-dagger)
+            abi.indexer(b, pooled, B, h, k1, heads=heads, idx=idx, val=val, ws=ws_i, events=events)
+            if kind == "dagger":  # fine stage: all-head rescoring of the k' candidates
+                abi.rerank(b, idx, k, idx=fin, val=fin_val, ws=ws_rr)
+        else:  # the dense DSA indexer
+            abi.score_topk(b, None, k, idx=idx, val=val, ws=ws_d, events=events)
+
+    def step_separate():  # the routed step as separate calls
         abi.route(b, pooled, B, h, 0, heads=heads, ws=ws_r)
-        abi.score_topk(b, heads, k, idx=idx, val=val, ws=ws_s)
+        abi.score_topk(b, heads, k1, idx=idx, val=val, ws=ws_s)
+        if kind == "dagger":
+            abi.rerank(b, idx, k, idx=fin, val=fin_val, ws=ws_rr)
 
     for _ in range(args.warmup):
         step()
@@ -169,32 +266,42 @@ def main(argv=None):
     # recorded on the launch stream right around that kernel (an event
     # between kernels costs a few microseconds, so it stays out of the
     # headline region)
+    sev = [(ev.create(), ev.create()) for _ in range(K)]
     for i in range(K):
         step(sev[i])
     torch.cuda.synchronize()
     score_ms = float(np.mean([ev.ms(a, c) for a, c in sev]))
-    # the same step as two calls (misa_route + misa_score_topk)
-    for _ in range(args.warmup):
-        step_separate()
-    ev.record(t_start, sp)
-    for _ in range(K):
-        step_separate()
-    ev.record(t_stop, sp)
-    torch.cuda.synchronize()
-    ms_sep = ev.ms(t_start, t_stop) / K
+    ms_sep = None
+    if routed:
+        for _ in range(args.warmup):
+            step_separate()
+        ev.record(t_start, sp)
+        for _ in range(K):
+            step_separate()
+        ev.record(t_stop, sp)
+        torch.cuda.synchronize()
+        ms_sep = ev.ms(t_start, t_stop) / K
     step()  # leave the fused call's outputs for the parity check
     torch.cuda.synchronize()
 
     n_keys = int((case["q_pos"].astype(np.int64) + 1).sum())
     value = n_keys / (ms_step * 1e-3)
-    alg_bytes = n_keys * KEY_BYTES + b.T * h * KEY_BYTES  # keys streamed + routed query rows
-    achieved = alg_bytes / (score_ms * 1e-3) / 1e9
-    traffic = traffic_for(args.workload)
-    # whole step: keys, complete pooled blocks and all head queries read;
-    # routed heads, selected ids and scores written
-    n_blocks = int((case["q_pos"].astype(np.int64) // B).sum())
-    step_bytes = (n_keys * KEY_BYTES + n_blocks * 128 * 4 + b.T * b.H * (KEY_BYTES + 4)
-                  + b.T * h * 4 + b.T * k * 8)
+    nh = h if routed else b.H
+    if kind == "prefill":
+        # dense MFMA contraction: 2 * 128 flops per (query, routed head, prefix key)
+        flops = 2.0 * 128 * nh * n_keys
+        achieved = flops / (score_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                "kernel": "score_prefill_kernel (32x32x16 bf16 MFMA, %d routed heads)" % nh,
+                "alg_flops_per_launch": flops}
+    else:
+        alg_bytes = n_keys * KEY_BYTES + b.T * nh * KEY_BYTES  # keys streamed + query rows
+        achieved = alg_bytes / (score_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(args.workload),
+                "kernel": "score_rows_kernel (%d-row head tiles, direct rows)" % (16 * ((nh + 15) // 16)),
+                "alg_bytes_per_launch": alg_bytes}
 
     res = {
         "metric": METRIC,
@@ -212,27 +319,41 @@ def main(argv=None):
         "config": {"workload": args.workload, "sequences": int(b.S), "context": int(b.Lmax),
                    "queries": int(b.T), "H_I": int(b.H), "B": B, "h": h, "k": k, "d": 128},
         "us_per_batch": ms_step * 1e3,
-        "us_per_batch_two_calls": ms_sep * 1e3,
-        "pool_us_once_per_cache": pool_us,
         "score_kernel_us": score_ms * 1e3,
         "wall_s_timed": wall,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "score_rows_kernel<1,false,4>",
-                     "alg_bytes_per_launch": alg_bytes},
-        "hbm_frac_whole_step": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": roof,
     }
+    if kind == "dagger":
+        res["config"]["k_prime"] = kc
+    if ms_sep is not None:
+        res["us_per_batch_separate_calls"] = ms_sep * 1e3
+    if pool_us is not None:
+        res["pool_us_once_per_cache"] = pool_us
+    if kind != "prefill":
+        # whole step: keys, complete pooled blocks and all head queries read;
+        # selected ids and scores written
+        n_blocks = int((case["q_pos"].astype(np.int64) // B).sum()) if routed else 0
+        step_bytes = (n_keys * KEY_BYTES + n_blocks * 128 * 4 + b.T * b.H * (KEY_BYTES + 4)
+                      + b.T * k1 * 8 + (b.T * kc * KEY_BYTES if kind == "dagger" else 0))
+        res["hbm_frac_whole_step"] = step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS
     if not args.no_cpu:
-        cv, cores, sample, out = cpu_baseline(case, cfg)
+        if kind == "prefill":  # a bounded sample: 16 query rows spread over the chunk
+            rows = np.linspace(0, b.T - 1, 16).astype(np.int64)
+            sample = "16 of %d query rows (evenly spaced), median of 3 runs" % b.T
+        else:
+            rows = np.arange(b.T)
+            sample = "all %d queries of the workload, median of 3 runs" % b.T
+        cv, cores, out = cpu_baseline_rows(case, cfg, rows)
         res["cpu_baseline"] = {"value": cv, "unit": "key-scores/s", "cores": cores,
                                "kind": "oracle", "sample": sample}
-        gi = idx.cpu().numpy()
-        gh = heads.cpu().numpy()
-        res["parity_vs_oracle"] = {
-            "heads_equal": bool(np.array_equal(np.sort(gh, 1), np.sort(out["heads"], 1))),
-            "set_overlap": float(np.mean([len(set(gi[t]) & set(out["idx"][t])) / k
-                                          for t in range(b.T)])),
-        }
+        gi = (fin if kind == "dagger" else idx).cpu().numpy()[rows]
+        par = {"rows_checked": int(len(rows)),
+               "set_overlap": float(np.mean([len(set(gi[i]) & set(out["idx"][i])) / k
+                                             for i in range(len(rows))]))}
+        if routed:
+            gh = heads.cpu().numpy()[rows]
+            par["heads_equal"] = bool(np.array_equal(np.sort(gh, 1), np.sort(out["heads"], 1)))
+        res["parity_vs_oracle"] = par
     print(json.dumps(res), flush=True)
     return 0
 

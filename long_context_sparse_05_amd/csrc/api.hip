@@ -82,6 +82,35 @@ int score_chunk(int rows, int ncols) {
   return (int)c;
 }
 
+// Many queries of one sequence with a few routed heads: the dense MFMA
+// tiling of prefill.hip.  Otherwise each query row streams the keys itself.
+constexpr int kPrefillMinRows = 64;
+bool use_prefill(const misa_batch *b, const int32_t *heads, int h) {
+  return heads && b->S == 1 && h <= 16 && b->T >= kPrefillMinRows;
+}
+
+PrefillArgs make_prefill_args(const misa_batch *b, const int32_t *heads, int h, float *scores) {
+  PrefillArgs p{};
+  p.keys = b->keys;
+  p.q = b->q;
+  p.w = b->w;
+  p.q_pos = b->q_pos;
+  p.heads = heads;
+  p.scores = scores;
+  p.seq = 0;
+  p.h = h;
+  p.H = b->H;
+  p.Lmax = b->Lmax;
+  p.T = b->T;
+  p.ld = b->Lmax;
+  // about 1024 workgroups: query tiles x key splits of a multiple of 64 keys
+  const int nqt = (b->T + prefill_queries_per_wg(h) - 1) / prefill_queries_per_wg(h);
+  const int nsplit = std::max(1, std::min((b->Lmax + 1023) / 1024, (1024 + nqt - 1) / nqt));
+  int split = (b->Lmax + nsplit - 1) / nsplit;
+  p.split = (split + 63) / 64 * 64;
+  return p;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? MISA_OK : MISA_ERR_HIP; }
 
 // zero the histograms -> [score rows + histogram | histogram] -> select.
@@ -240,6 +269,9 @@ int misa_score(const misa_batch *b, const int32_t *heads, int32_t h, float *scor
   if (rc) return rc;
   if (!scores) return MISA_ERR_NULL;
   if (heads && (h < 1 || h > b->H)) return MISA_ERR_SHAPE;
+  if (use_prefill(b, heads, h))
+    return hip_status(launch_score_prefill(make_prefill_args(b, heads, h, scores),
+                                           (hipStream_t)stream));
   ScoreArgs s = make_score_args(b, heads, heads ? h : b->H);
   s.scores = scores;
   s.hist = nullptr;
@@ -271,6 +303,17 @@ int misa_score_topk_ev(const misa_batch *b, const int32_t *heads, int32_t h, int
   if (k < 1 || k > b->Lmax) return MISA_ERR_SHAPE;
   const SelectLayout L = select_layout(b->T, b->Lmax, k, true);
   if (ws_bytes < L.total) return MISA_ERR_WORKSPACE;
+  if (use_prefill(b, heads, h)) {
+    float *sc = (float *)((char *)ws + L.scores);
+    if (ev_start && hipEventRecord((hipEvent_t)ev_start, (hipStream_t)stream) != hipSuccess)
+      return MISA_ERR_HIP;
+    if (launch_score_prefill(make_prefill_args(b, heads, h, sc), (hipStream_t)stream) != hipSuccess)
+      return MISA_ERR_HIP;
+    if (ev_stop && hipEventRecord((hipEvent_t)ev_stop, (hipStream_t)stream) != hipSuccess)
+      return MISA_ERR_HIP;
+    return run_select(nullptr, sc, b->T, b->Lmax, b->q_pos, 1, nullptr, k, idx, val, ws, L,
+                      (hipStream_t)stream);
+  }
   ScoreArgs s = make_score_args(b, heads, heads ? h : b->H);
   s.scores = (float *)((char *)ws + L.scores);
   s.cand = nullptr;
@@ -308,6 +351,17 @@ int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t
   ra.zero_hist = (uint32_t *)((char *)sws + L.hist);
   ra.zero_ctr = (uint32_t *)((char *)sws + L.counters);
   if (launch_route(ra, (hipStream_t)stream) != hipSuccess) return MISA_ERR_HIP;
+  if (use_prefill(b, heads, h)) {
+    float *sc = (float *)((char *)sws + L.scores);
+    if (ev_start && hipEventRecord((hipEvent_t)ev_start, (hipStream_t)stream) != hipSuccess)
+      return MISA_ERR_HIP;
+    if (launch_score_prefill(make_prefill_args(b, heads, h, sc), (hipStream_t)stream) != hipSuccess)
+      return MISA_ERR_HIP;
+    if (ev_stop && hipEventRecord((hipEvent_t)ev_stop, (hipStream_t)stream) != hipSuccess)
+      return MISA_ERR_HIP;
+    return run_select(nullptr, sc, b->T, b->Lmax, b->q_pos, 1, nullptr, k, idx, val, sws, L,
+                      (hipStream_t)stream, nullptr, nullptr, true);
+  }
   ScoreArgs s = make_score_args(b, heads, h);
   s.scores = (float *)((char *)sws + L.scores);
   s.cand = nullptr;

@@ -23,6 +23,21 @@ struct ScoreArgs {
 };
 hipError_t launch_score_rows(const ScoreArgs &a, hipStream_t st);
 
+// Routed scoring of many queries of one sequence (prefill.hip).
+struct PrefillArgs {
+  const uint16_t *keys;    // bf16 [S][Lmax][128]
+  const uint16_t *q;       // bf16 [T][H][128]
+  const float *w;          // [T][H]
+  const int32_t *q_pos;    // [T]
+  const int32_t *heads;    // [T][h], h <= 16
+  float *scores;           // [T][ld]
+  int seq;                 // the one sequence all rows read
+  int h, H, Lmax, T, ld;
+  int split;               // key columns per workgroup, a multiple of 64
+};
+hipError_t launch_score_prefill(const PrefillArgs &a, hipStream_t st);
+int prefill_queries_per_wg(int h);
+
 // Per-row top-k selection (topk.hip).
 struct TopkArgs {
   const float *scores;     // [rows][ld]

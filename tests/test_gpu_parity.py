@@ -327,3 +327,79 @@ def test_indexer_fused_equals_separate_calls(S, Lmax, T, H, seed, mode):
         if sorted(gi[t]) != sorted(om["idx"][t]):
             parity.check_set(gi[t], om["idx"][t], lambda i: om["scores"][t, i], n, k,
                              parity.row_sbar(om["scores"][t], n))
+
+
+# ------------------------------------------------------- prefill tiling path
+PREFILL_CASES = [
+    # Lmax, T, H, h, positions
+    (3000, 200, 32, 8, "tail"),
+    (1100, 97, 8, 3, "random"),
+    (2500, 130, 32, 16, "random"),
+    (700, 64, 16, 1, "tail"),
+    (4200, 256, 64, 8, "tail"),
+]
+
+
+def make_prefill(Lmax, T, H, seed, positions):
+    rng = np.random.default_rng(seed + 5)
+    if positions == "tail":
+        q_pos = np.arange(Lmax - T, Lmax, dtype=np.int32)
+    else:
+        q_pos = np.sort(rng.integers(0, Lmax, size=T)).astype(np.int32)
+    return synth.random_case(1, Lmax, T, H, seed=seed, q_pos=q_pos,
+                             q_seq=np.zeros(T, np.int32))
+
+
+@pytest.mark.parametrize("Lmax,T,H,h,positions", PREFILL_CASES)
+def test_prefill_scores_and_selection(Lmax, T, H, h, positions):
+    """Many queries of one sequence with h <= 16 routed heads take the
+    32x32 MFMA tiling; scores, selections and the fused call all match the
+    oracle."""
+    abi = _abi()
+    case = make_prefill(Lmax, T, H, 11, positions)
+    b = upload(case)
+    ob = orc.Batch.from_case(case)
+    rng = np.random.default_rng(Lmax + T)
+    heads = np.stack([rng.permutation(H)[:h] for _ in range(T)]).astype(np.int32)
+    th = torch.from_numpy(heads).cuda()
+    got = np_(abi.score(b, th))
+    osc = orc.scores(ob, heads)
+    parity.check_scores(got, osc, n_valid(case))
+    k = min(257, Lmax)
+    idx, val = abi.score_topk(b, th, k)
+    idx, val = np_(idx), np_(val)
+    oidx = np.stack([orc.topk(osc[t, :n_valid(case)[t]], k)[0] for t in range(T)])
+    for t in range(T):
+        n = int(n_valid(case)[t])
+        parity.check_exact_topk(idx[t], val[t], got[t], n, k, orc.topk_f32)
+        parity.check_set(idx[t], oidx[t], lambda i: osc[t, i], n, k, parity.row_sbar(osc[t], n))
+    # the fused call routes first; compare with route + score_topk
+    B = 64
+    pooled = abi.pool(b, B)
+    rh = abi.route(b, pooled, B, h, 0)
+    ri, rv = abi.score_topk(b, rh, k)
+    fh, fi, fv = abi.indexer(b, pooled, B, h, k)
+    assert np.array_equal(np_(fh), np_(rh))
+    assert [set(r) for r in np_(fi)] == [set(r) for r in np_(ri)]
+
+
+def test_prefill_integer_inputs_bit_exact():
+    abi = _abi()
+    T, Lmax, H, h = 96, 1500, 16, 8
+    q_pos = np.arange(Lmax - T, Lmax, dtype=np.int32)
+    case = synth.random_case(1, Lmax, T, H, seed=3, dist="int", q_pos=q_pos,
+                             q_seq=np.zeros(T, np.int32))
+    b = upload(case)
+    ob = orc.Batch.from_case(case)
+    rng = np.random.default_rng(9)
+    heads = np.stack([rng.permutation(H)[:h] for _ in range(T)]).astype(np.int32)
+    th = torch.from_numpy(heads).cuda()
+    got = np_(abi.score(b, th))
+    osc = orc.scores(ob, heads)
+    for t in range(T):
+        n = int(q_pos[t]) + 1
+        assert np.array_equal(got[t, :n].astype(np.float64), osc[t, :n])
+        assert np.all(np.isneginf(got[t, n:]))
+    idx, _ = abi.score_topk(b, th, 300)
+    oidx = np.stack([orc.topk(osc[t, :q_pos[t] + 1], 300)[0] for t in range(T)])
+    assert [set(r) for r in np_(idx)] == [set(r) for r in oidx]
