@@ -34,6 +34,16 @@ int check_batch(const misa_batch *b, bool need_q) {
   return MISA_OK;
 }
 
+int hist_chunk(int rows, int ncols) {
+  // about 1024 workgroups; many rows -> whole rows per workgroup, so each
+  // non-empty bin is merged into the row histogram once
+  const size_t work = (size_t)rows * ncols;
+  size_t c = (work + 1023) / 1024;
+  c = (c + 255) / 256 * 256;
+  c = std::max<size_t>(4096, std::min<size_t>((size_t)ncols, c));
+  return (int)c;
+}
+
 int filter_chunk(int rows, int ncols) {
   // about 512 filter workgroups, each a multiple of 4096 columns (one round)
   const int per_row = std::max(1, 512 / std::max(1, rows));
@@ -86,7 +96,7 @@ int score_chunk(int rows, int ncols) {
 // tiling of prefill.hip.  Otherwise each query row streams the keys itself.
 constexpr int kPrefillMinRows = 64;
 bool use_prefill(const misa_batch *b, const int32_t *heads, int h) {
-  return heads && b->S == 1 && h <= 16 && b->T >= kPrefillMinRows;
+  return heads && b->S == 1 && b->T >= kPrefillMinRows && prefill_supported(h, b->Lmax);
 }
 
 PrefillArgs make_prefill_args(const misa_batch *b, const int32_t *heads, int h, float *scores) {
@@ -103,24 +113,29 @@ PrefillArgs make_prefill_args(const misa_batch *b, const int32_t *heads, int h, 
   p.Lmax = b->Lmax;
   p.T = b->T;
   p.ld = b->Lmax;
-  // about 1024 workgroups: query tiles x key splits of a multiple of 64 keys
+  // about 1024 workgroups: query tiles x key splits of whole key tiles
   const int nqt = (b->T + prefill_queries_per_wg(h) - 1) / prefill_queries_per_wg(h);
   const int nsplit = std::max(1, std::min((b->Lmax + 1023) / 1024, (1024 + nqt - 1) / nqt));
   int split = (b->Lmax + nsplit - 1) / nsplit;
-  p.split = (split + 63) / 64 * 64;
+  p.split = (split + kPrefillKeyTile - 1) / kPrefillKeyTile * kPrefillKeyTile;
   return p;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MISA_OK : MISA_ERR_HIP; }
 
-// zero the histograms -> [score rows + histogram | histogram] -> select.
+// Selection over rows of ld columns.  Few rows: zero the histograms ->
+// [score rows + histogram | histogram] -> multi-workgroup filter -> finish.
+// Enough rows to fill the GPU: [score rows] -> one workgroup per row.
+constexpr int kRowSelectMinRows = 256;
+
 int run_select(const ScoreArgs *score, const float *scores_in, int rows, int ld,
                const int32_t *row_len, int row_len_add, const int32_t *map, int k,
                int32_t *idx, float *val, void *ws, const SelectLayout &L, hipStream_t st,
                void *ev_start = nullptr, void *ev_stop = nullptr, bool zeroed = false) {
+  const bool row_mode = rows >= kRowSelectMinRows;
   uint32_t *hist = (uint32_t *)((char *)ws + L.hist);
   hipError_t e = hipSuccess;
-  if (!zeroed) {  // the fused indexer call clears these in its router kernel
+  if (!zeroed && !row_mode) {  // the fused indexer call clears these in its router kernel
     e = launch_fill_u32(hist, (L.cand - L.hist) / sizeof(uint32_t), 0u, st);
     if (e != hipSuccess) return MISA_ERR_HIP;
   }
@@ -140,15 +155,17 @@ int run_select(const ScoreArgs *score, const float *scores_in, int rows, int ld,
   t.k = k;
   if (score) {
     ScoreArgs s = *score;
-    s.hist = hist;
+    s.hist = row_mode ? nullptr : hist;
     if (ev_start && hipEventRecord((hipEvent_t)ev_start, st) != hipSuccess) return MISA_ERR_HIP;
     e = launch_score_rows(s, st);
     if (e == hipSuccess && ev_stop) e = hipEventRecord((hipEvent_t)ev_stop, st);
-  } else {
-    t.chunk = score_chunk(rows, ld);
-    e = launch_topk_hist(t, hist, st);
+    if (e != hipSuccess) return MISA_ERR_HIP;
   }
-  if (e != hipSuccess) return MISA_ERR_HIP;
+  if (row_mode) return hip_status(launch_topk_rowselect(t, st));
+  if (!score) {
+    t.chunk = hist_chunk(rows, ld);
+    if ((e = launch_topk_hist(t, hist, st)) != hipSuccess) return MISA_ERR_HIP;
+  }
   t.chunk = filter_chunk(rows, ld);
   if ((e = launch_topk_select(t, st)) != hipSuccess) return MISA_ERR_HIP;
   return MISA_OK;

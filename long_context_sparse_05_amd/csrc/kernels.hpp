@@ -35,8 +35,11 @@ struct PrefillArgs {
   int h, H, Lmax, T, ld;
   int split;               // key columns per workgroup, a multiple of 64
 };
+// key tile of the prefill kernel: PrefillArgs::split must be a multiple
+constexpr int kPrefillKeyTile = 128;
 hipError_t launch_score_prefill(const PrefillArgs &a, hipStream_t st);
 int prefill_queries_per_wg(int h);
+bool prefill_supported(int h, int ld);  // the launch shape fits h and the row length
 
 // Per-row top-k selection (topk.hip).
 struct TopkArgs {
@@ -54,6 +57,7 @@ struct TopkArgs {
 };
 hipError_t launch_topk_hist(const TopkArgs &a, uint32_t *hist, hipStream_t st);
 hipError_t launch_topk_select(const TopkArgs &a, hipStream_t st);
+hipError_t launch_topk_rowselect(const TopkArgs &a, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t st);
 
 // Block mean-pool (pool.hip).

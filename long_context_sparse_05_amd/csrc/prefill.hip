@@ -13,10 +13,19 @@
 // accumulator r, query g*(16/HP) + r/HP and head slot r%HP.  The weighted
 // ReLU head reduction is therefore a register-local sum, with no cross-lane
 // traffic.  A workgroup owns QWG consecutive queries x one split of the key
-// range; keys stream through a double-buffered LDS tile of 64 keys (rows
+// range; keys stream through a double-buffered LDS tile of 128 keys (rows
 // padded to 272 bytes), loaded with coalesced 16-byte loads one tile ahead.
+// Within a tile each wave pipelines its 32-key column blocks: the MFMA chain
+// of the next block is issued before the epilogue of the previous one.
 // Key tiles beyond the workgroup's last query position are skipped
-// (causality); columns past a query's position are written as -inf.
+// (causality); columns past a query's position are written as -inf.  The
+// epilogue is kept lean because on CDNA every wave64 VALU op costs four
+// cycles against 32 for one 32x32x16 MFMA: the first MFMA of each chain
+// takes a zero accumulator, store addresses are per-row pointers set up
+// once, and tiles below every query's position store without a mask.
+#include <climits>
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -28,35 +37,50 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-constexpr int kPfKeys = 64;       // keys per LDS tile
 constexpr int kPfRowLds = 272;    // bytes per key row in LDS (256 + 16)
-constexpr int kPfWaves = 4;
 
-template <int HP, int RT>
-__global__ __launch_bounds__(kPfWaves * 64) void score_prefill_kernel(PrefillArgs a) {
+template <int HP, int RT, int NW, int KT>
+__global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a) {
   constexpr int QPT = 32 / HP;                  // queries per 32-row tile
   constexpr int QPL = 16 / HP;                  // queries per lane (per tile)
-  constexpr int QWG = kPfWaves * RT * QPT;      // queries per workgroup
-  __shared__ uint4 ktile[2][kPfKeys * kPfRowLds / 16];
-  __shared__ int sh_pmax;
+  constexpr int QWG = NW * RT * QPT;            // queries per workgroup
+  constexpr int NT = NW * 64;
+  constexpr int LPT = KT * 16 / NT;             // 16-byte key loads per thread per tile
+  static_assert(LPT * NT == KT * 16, "tile load split");
+  __shared__ uint4 ktile[2][KT * kPfRowLds / 16];
+  __shared__ int sh_pmax, sh_pmin;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   const int qt0 = blockIdx.y * QWG;
   const int k0 = blockIdx.x * a.split;
   const int k1 = min(k0 + a.split, a.Lmax);
 
-  // last position of the workgroup's queries: keys past it are never needed
-  if (tid == 0) sh_pmax = -1;
+  // positions of the workgroup's queries: keys past the last one are never
+  // needed; tiles below the first one need no causal mask
+  if (tid == 0) {
+    sh_pmax = -1;
+    sh_pmin = 0x7FFFFFFF;
+  }
   __syncthreads();
-  if (tid < QWG && qt0 + tid < a.T) atomicMax(&sh_pmax, a.q_pos[qt0 + tid]);
+  if (tid < QWG && qt0 + tid < a.T) {
+    const int p = a.q_pos[qt0 + tid];
+    atomicMax(&sh_pmax, p);
+    atomicMin(&sh_pmin, p);
+  }
   __syncthreads();
   const int kend = min(k1, sh_pmax + 1);
+  const bool all_rows = qt0 + QWG <= a.T;
+  const int kfull = all_rows ? min(k1, sh_pmin + 1) : 0;  // [k0, kfull): no mask
 
   // A fragments: row l32 of tile rt holds (query, head slot) of the layout above
   bf16x8 qa[RT][8];
   float wv[RT][16];
-  int tq[RT][QPL];   // this lane's queries (row ids), -1 when past T
-  int pq[RT][QPL];   // their positions
+  // this lane's query rows of the score matrix, as byte offsets from the
+  // workgroup's first row (at most QWG rows of ld floats: 32 bits suffice),
+  // and their positions (INT_MIN past T: nothing is stored for such rows)
+  char *const wg_rows = (char *)(a.scores + (size_t)qt0 * a.ld);
+  uint32_t rowo[RT][QPL];
+  int pq[RT][QPL];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int tile_q0 = qt0 + (wave * RT + rt) * QPT;
@@ -82,78 +106,125 @@ __global__ __launch_bounds__(kPfWaves * 64) void score_prefill_kernel(PrefillArg
 #pragma unroll
     for (int qq = 0; qq < QPL; ++qq) {
       const int t = tile_q0 + g * QPL + qq;
-      tq[rt][qq] = t < a.T ? t : -1;
-      pq[rt][qq] = t < a.T ? a.q_pos[t] : -1;
+      rowo[rt][qq] = (uint32_t)(((t - qt0) * a.ld + l32) * 4);
+      pq[rt][qq] = t < a.T ? a.q_pos[t] : INT_MIN;
     }
   }
 
-  // coalesced tile load: thread = (key lane tid/16, 16-byte slice tid%16), 4 rounds
+  // coalesced tile load: thread = (key lane tid/16, 16-byte slice tid%16)
   const uint16_t *kseq = a.keys + (size_t)a.seq * a.Lmax * kD;
-  auto load_tile = [&](int kt, uint4 (&kr)[4]) {
+  auto load_tile = [&](int kt, uint4 (&kr)[LPT]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kt + 16 * i + (tid >> 4);
+    for (int i = 0; i < LPT; ++i) {
+      const int key = kt + (NT / 16) * i + (tid >> 4);
       kr[i] = key < kend ? load_nt16(kseq + (size_t)key * kD + (tid & 15) * 8)
                          : make_uint4(0, 0, 0, 0);
     }
   };
-  uint4 kr[4];
+  const f32x16 zero = {};
+  uint4 kr[LPT];
   if (k0 < kend) load_tile(k0, kr);
   int buf = 0;
-  for (int kt = k0; kt < kend; kt += kPfKeys, buf ^= 1) {
+  for (int kt = k0; kt < kend; kt += KT, buf ^= 1) {
     char *lt = (char *)ktile[buf];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *(uint4 *)(lt + (16 * i + (tid >> 4)) * kPfRowLds + (tid & 15) * 16) = kr[i];
+    for (int i = 0; i < LPT; ++i)
+      *(uint4 *)(lt + ((NT / 16) * i + (tid >> 4)) * kPfRowLds + (tid & 15) * 16) = kr[i];
     __syncthreads();
-    if (kt + kPfKeys < kend) load_tile(kt + kPfKeys, kr);  // in flight during the MFMAs
+    if (kt + KT < kend) load_tile(kt + KT, kr);  // in flight during the MFMAs
+    // software pipeline over the tile's 32-key column blocks: the MFMA chain
+    // of block c+1 is issued before the epilogue of block c, so the vector
+    // ALU work overlaps the matrix core.  Tiles below every query's position
+    // (FULL) take a straight-line body with unmasked stores.
+    auto tile_body = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      auto chain = [&](int cb, f32x16 (&acc)[RT]) {
+        const char *kr0 = lt + (cb * 32 + l32) * kPfRowLds + g * 16;
+        {
+          const uint4 bv = *(const uint4 *)kr0;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      f32x16 acc[RT];
+          for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32(qa[rt][0], as_bf16x8(bv), zero);
+        }
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
+        for (int s = 1; s < 8; ++s) {
+          const uint4 bv = *(const uint4 *)(kr0 + s * 32);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[rt][r] = 0.f;
+          for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32(qa[rt][s], as_bf16x8(bv), acc[rt]);
+        }
+      };
+      auto epilogue = [&](int cb, const f32x16 (&acc)[RT]) {
+        const int kb = kt + cb * 32;  // this lane's key is kb + l32
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const uint4 bv = *(const uint4 *)(lt + (half * 32 + l32) * kPfRowLds + s * 32 + g * 16);
+        for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32(qa[rt][s], as_bf16x8(bv), acc[rt]);
-      }
-      const int key = kt + half * 32 + l32;
+          for (int qq = 0; qq < QPL; ++qq) {
+            // ReLU as a signed-integer max of the bits: negative floats
+            // (and -0) have the sign bit set, so they become +0
+            float sc = wv[rt][qq * HP] * __int_as_float(max(__float_as_int(acc[rt][qq * HP]), 0));
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
+            for (int hs = 1; hs < HP; ++hs)
+              sc += wv[rt][qq * HP + hs] * __int_as_float(max(__float_as_int(acc[rt][qq * HP + hs]), 0));
+            float *dst = (float *)(wg_rows + (size_t)kb * 4 + rowo[rt][qq]);
+            if (FULL) {
+              *dst = sc;
+            } else if (pq[rt][qq] != INT_MIN && kb + l32 < k1) {
+              *dst = kb + l32 <= pq[rt][qq] ? sc : -INFINITY;
+            }
+          }
+        }
+      };
+      f32x16 acc0[RT], acc1[RT];
+      chain(0, acc0);
 #pragma unroll
-        for (int qq = 0; qq < QPL; ++qq) {
-          float sc = 0.f;
-#pragma unroll
-          for (int hs = 0; hs < HP; ++hs) sc += wv[rt][qq * HP + hs] * fmaxf(acc[rt][qq * HP + hs], 0.f);
-          const int t = tq[rt][qq];
-          if (t >= 0 && key < k1) a.scores[(size_t)t * a.ld + key] = key <= pq[rt][qq] ? sc : -INFINITY;
+      for (int cb = 1; cb < KT / 32; ++cb) {
+        if (cb & 1) {
+          chain(cb, acc1);
+          epilogue(cb - 1, acc0);
+        } else {
+          chain(cb, acc0);
+          epilogue(cb - 1, acc1);
         }
       }
-    }
+      if ((KT / 32) & 1) epilogue(KT / 32 - 1, acc0); else epilogue(KT / 32 - 1, acc1);
+    };
+    if (kt + KT <= kfull)  // uniform
+      tile_body(std::true_type{});
+    else
+      tile_body(std::false_type{});
   }
   // columns of this split past every query of the workgroup
   for (int qi = 0; qi < QWG; ++qi) {
     const int t = qt0 + qi;
     if (t >= a.T) break;
-    for (int c = max(kend, k0) + tid; c < k1; c += kPfWaves * 64) a.scores[(size_t)t * a.ld + c] = -INFINITY;
+    for (int c = max(kend, k0) + tid; c < k1; c += NT) a.scores[(size_t)t * a.ld + c] = -INFINITY;
   }
 }
 
+constexpr int kPfWaves = 8, kPfKeys = kPrefillKeyTile;
+// row tiles per wave: two where a lane's rows are few whole head sets; one
+// where a lane holds many queries (HP <= 2), whose row pointers would not
+// fit in registers beside two pipelined accumulator sets
+constexpr int pf_rt(int hp) { return hp >= 4 ? 2 : 1; }
+
 template <int HP>
 static hipError_t launch_hp(const PrefillArgs &a, hipStream_t st) {
-  constexpr int RT = 2;
+  constexpr int RT = pf_rt(HP);
   constexpr int QWG = kPfWaves * RT * (32 / HP);
+  if (a.split % kPfKeys) return hipErrorInvalidValue;
+  if ((uint64_t)QWG * a.ld * 4 > 0xFFFFFFFFull) return hipErrorInvalidValue;  // 32-bit row offsets
   dim3 grid((a.Lmax + a.split - 1) / a.split, (a.T + QWG - 1) / QWG);
-  hipLaunchKernelGGL((score_prefill_kernel<HP, RT>), grid, dim3(kPfWaves * 64), 0, st, a);
+  hipLaunchKernelGGL((score_prefill_kernel<HP, RT, kPfWaves, kPfKeys>), grid,
+                     dim3(kPfWaves * 64), 0, st, a);
   return hipGetLastError();
+}
+
+bool prefill_supported(int h, int ld) {
+  return h >= 1 && h <= 16 && (uint64_t)prefill_queries_per_wg(h) * ld * 4 <= 0xFFFFFFFFull;
 }
 
 int prefill_queries_per_wg(int h) {
   const int hp = h <= 1 ? 1 : h <= 2 ? 2 : h <= 4 ? 4 : h <= 8 ? 8 : 16;
-  return kPfWaves * 2 * (32 / hp);
+  return kPfWaves * pf_rt(hp) * (32 / hp);
 }
 
 hipError_t launch_score_prefill(const PrefillArgs &a, hipStream_t st) {

@@ -124,6 +124,8 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a) {
   int32_t *irow = a.idx + (size_t)r * a.k;
   float *vrow = a.val ? a.val + (size_t)r * a.k : nullptr;
   uint2 *crow = a.cand + (size_t)r * a.cap;
+  const bool solo = gridDim.x == 1;
+  uint32_t run_sel = 0, run_cnd = 0;
   for (int sb = c0; sb < c1; sb += kSub) {  // uniform trip count
     if (sb != c0) load_round(sb, sv);
     uint32_t fs = 0, fc = 0;  // this thread's 16 columns: above b1 / equal to b1
@@ -142,11 +144,19 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a) {
     const uint32_t mine = ((uint32_t)__popc(fs) << 16) | (uint32_t)__popc(fc);
     uint32_t total;
     const uint32_t excl = block_scan<256>(mine, sh, total) - mine;
-    // one global atomic per counter per round reserves this workgroup's range
+    // one global atomic per counter per round reserves this workgroup's range;
+    // a workgroup that owns the whole row keeps its own running offsets
     if (tid == 0) {
-      sh[8] = (total >> 16) ? atomicAdd(&cnt[0], total >> 16) : 0u;
-      sh[9] = (total & 0xFFFFu) ? atomicAdd(&cnt[1], total & 0xFFFFu) : 0u;
+      if (solo) {
+        sh[8] = run_sel;
+        sh[9] = run_cnd;
+      } else {
+        sh[8] = (total >> 16) ? atomicAdd(&cnt[0], total >> 16) : 0u;
+        sh[9] = (total & 0xFFFFu) ? atomicAdd(&cnt[1], total & 0xFFFFu) : 0u;
+      }
     }
+    run_sel += total >> 16;
+    run_cnd += total & 0xFFFFu;
     __syncthreads();
     uint32_t so = sh[8] + (excl >> 16), co = sh[9] + (excl & 0xFFFFu);
 #pragma unroll
@@ -172,50 +182,18 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a) {
   }
 }
 
-// ------------------------------------------------------------------- finish
-template <bool MAP>
-__global__ __launch_bounds__(kSelThreads) void topk_finish_kernel(TopkArgs a) {
-  constexpr int NT = kSelThreads;
-  constexpr int NW = NT / kWave;
-  __shared__ uint64_t cs[kSelCap];
-  __shared__ uint64_t cs2[kSelCompact];
-  __shared__ uint32_t hs[256];
-  __shared__ uint32_t sh[NW + 16];  // [0, NW) scan scratch, then counters and pass results
-  uint32_t *ctr = sh + NW;          // [0] next output slot [1] compacted
-  uint32_t *res = sh + NW + 4;      // [0] digit [1] count above it [2] count in it
-  const int r = blockIdx.x;
+// Resolve the candidates of the threshold digit: 8-bit digit passes over
+// LDS histograms of the remaining 52 composite-key bits, emitting every key
+// above each pass's crossing digit (wave-aggregated LDS atomics for the
+// output slots, starting at ctr[0]) and compacting the survivors, until the
+// crossing bin holds exactly the keys still needed.  Candidates come from
+// `cur` (keep) or are re-read from the score row (more than fit in LDS).
+template <bool MAP, int NT>
+__device__ __forceinline__ void resolve_candidates(
+    uint64_t *cur, int ncur, bool keep, int n, const float *srow, const int32_t *mrow,
+    const Thresh th, int32_t *irow, float *vrow, uint64_t *cs, uint64_t *cs2, uint32_t *hs,
+    uint32_t *sh, uint32_t *ctr, uint32_t *res) {
   const int tid = threadIdx.x;
-  const uint32_t *cnt = a.counters + (size_t)r * kRowCounters;
-  Thresh th;
-  th.b1 = (int)cnt[4];
-  th.above = cnt[5];
-  th.eq = cnt[6];
-  th.kk = cnt[7];
-
-  int32_t *irow = a.idx + (size_t)r * a.k;
-  float *vrow = a.val ? a.val + (size_t)r * a.k : nullptr;
-  for (int i = (int)th.kk + tid; i < a.k; i += NT) {
-    irow[i] = -1;
-    if (vrow) vrow[i] = -INFINITY;
-  }
-  if (th.kk == 0) return;  // uniform
-
-  const int n = row_valid_len(a, r);
-  const float *srow = a.scores + (size_t)r * a.ld;
-  const int32_t *mrow = MAP ? a.map + (size_t)r * a.ld : nullptr;
-  const bool keep = th.eq <= (uint32_t)a.cap;
-  uint64_t *cur = cs;
-  int ncur = keep ? (int)min(th.eq, (uint32_t)a.cap) : 0;
-  if (keep) {
-    const uint2 *crow = a.cand + (size_t)r * a.cap;
-    for (int i = tid; i < ncur; i += NT) {
-      const uint2 e = crow[i];
-      cs[i] = composite(e.x, MAP ? mrow[e.y] : (int)e.y);
-    }
-  }
-  if (tid == 0) ctr[0] = th.above;
-  __syncthreads();
-
   // Visit every candidate that matches (prefix, mask) in uniform rounds of NT
   // (wave ballots stay legal): from LDS, or (too many ties) from the row.
   auto for_each = [&](uint64_t prefix, uint64_t mask, auto &&fn) {
@@ -296,6 +274,208 @@ __global__ __launch_bounds__(kSelThreads) void topk_finish_kernel(TopkArgs a) {
   }
 }
 
+// ------------------------------------------------------------------- finish
+template <bool MAP>
+__global__ __launch_bounds__(kSelThreads) void topk_finish_kernel(TopkArgs a) {
+  constexpr int NT = kSelThreads;
+  constexpr int NW = NT / kWave;
+  __shared__ uint64_t cs[kSelCap];
+  __shared__ uint64_t cs2[kSelCompact];
+  __shared__ uint32_t hs[256];
+  __shared__ uint32_t sh[NW + 16];  // [0, NW) scan scratch, then counters and pass results
+  uint32_t *ctr = sh + NW;          // [0] next output slot [1] compacted
+  uint32_t *res = sh + NW + 4;      // [0] digit [1] count above it [2] count in it
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint32_t *cnt = a.counters + (size_t)r * kRowCounters;
+  Thresh th;
+  th.b1 = (int)cnt[4];
+  th.above = cnt[5];
+  th.eq = cnt[6];
+  th.kk = cnt[7];
+
+  int32_t *irow = a.idx + (size_t)r * a.k;
+  float *vrow = a.val ? a.val + (size_t)r * a.k : nullptr;
+  for (int i = (int)th.kk + tid; i < a.k; i += NT) {
+    irow[i] = -1;
+    if (vrow) vrow[i] = -INFINITY;
+  }
+  if (th.kk == 0) return;  // uniform
+
+  const int n = row_valid_len(a, r);
+  const float *srow = a.scores + (size_t)r * a.ld;
+  const int32_t *mrow = MAP ? a.map + (size_t)r * a.ld : nullptr;
+  const bool keep = th.eq <= (uint32_t)a.cap;
+  const int ncur = keep ? (int)min(th.eq, (uint32_t)a.cap) : 0;
+  if (keep) {
+    const uint2 *crow = a.cand + (size_t)r * a.cap;
+    for (int i = tid; i < ncur; i += NT) {
+      const uint2 e = crow[i];
+      cs[i] = composite(e.x, MAP ? mrow[e.y] : (int)e.y);
+    }
+  }
+  if (tid == 0) ctr[0] = th.above;
+  __syncthreads();
+
+  resolve_candidates<MAP, NT>(cs, ncur, keep, n, srow, mrow, th, irow, vrow, cs, cs2, hs, sh, ctr, res);
+}
+
+// --------------------------------------------------------------- row select
+// With enough rows to fill the GPU, one 1024-thread workgroup per row does
+// the whole selection: pass 1 builds the row's first-digit histogram in LDS,
+// pass 2 writes the columns above the threshold digit and collects the
+// digit's candidates in LDS, and the candidates are resolved.  No global
+// atomics and no zeroed workspace.  Rows of at most kRegCols columns (REG)
+// are read from HBM once: each thread keeps its 64 scores in registers from
+// pass 1 to pass 2.  Longer rows are streamed twice.
+constexpr int kSelU = 4;                                    // float4 loads per thread per round
+constexpr int kSelRound = kSelThreads * 4 * kSelU;          // columns per round
+constexpr int kRegRounds = 4;
+constexpr int kRegCols = kSelRound * kRegRounds;            // 65536
+
+template <bool MAP, bool REG>
+__global__ __launch_bounds__(kSelThreads) void topk_rowselect_kernel(TopkArgs a) {
+  constexpr int NT = kSelThreads;
+  constexpr int NW = NT / kWave;
+  constexpr int U = kSelU;
+  constexpr int RR = REG ? kRegRounds : 1;  // rounds held in registers
+  __shared__ uint64_t cs[kSelCap];
+  __shared__ uint64_t cs2[kSelCompact];
+  __shared__ uint32_t hs[256];
+  __shared__ uint32_t sh[NW + 16];
+  uint32_t *ctr = sh + NW;       // [0] next output slot [1] compacted
+  uint32_t *res = sh + NW + 4;   // [0] digit [1] count above it [2] count in it
+  __shared__ unsigned long long cnt64;  // (above emitted << 32) | candidates collected
+  uint32_t *lh = (uint32_t *)cs;  // pass-1 histogram lives in the candidate array
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n = row_valid_len(a, r);
+  const float *srow = a.scores + (size_t)r * a.ld;
+  const int32_t *mrow = MAP ? a.map + (size_t)r * a.ld : nullptr;
+  const bool vec = (a.ld % 4) == 0;
+
+  auto load_round = [&](int base, float (&sv)[U][4]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int cf = base + u * NT * 4 + 4 * tid;
+      if (vec && cf + 3 < n) {
+        const float4 x = *(const float4 *)(srow + cf);
+        sv[u][0] = x.x; sv[u][1] = x.y; sv[u][2] = x.z; sv[u][3] = x.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[u][e] = cf + e < n ? srow[cf + e] : 0.f;
+      }
+    }
+  };
+  auto valid_col = [&](int c) { return c < n && (!MAP || mrow[c] >= 0); };
+  auto hist_round = [&](int base, const float (&sv)[U][4]) {
+    const bool all = !MAP && base + kSelRound <= n;  // uniform: no per-column test
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (all || valid_col(base + u * NT * 4 + 4 * tid + e))
+          atomicAdd(&lh[order_key(sv[u][e]) >> kHistShift], 1u);
+  };
+
+  for (int i = tid; i < kHistBins; i += NT) lh[i] = 0;
+  __syncthreads();
+  float sv[RR][U][4];
+  if (REG) {  // pass 1: every load of the row in flight, then the histogram
+#pragma unroll
+    for (int rr = 0; rr < RR; ++rr)
+      if (rr * kSelRound < n) load_round(rr * kSelRound, sv[rr]);
+#pragma unroll
+    for (int rr = 0; rr < RR; ++rr)
+      if (rr * kSelRound < n) hist_round(rr * kSelRound, sv[rr]);
+  } else {
+    for (int base = 0; base < n; base += kSelRound) {
+      load_round(base, sv[0]);
+      hist_round(base, sv[0]);
+    }
+  }
+  __syncthreads();
+  const Thresh th = threshold_from_lds<NT>(lh, (uint32_t)a.k, sh);
+  int32_t *irow = a.idx + (size_t)r * a.k;
+  float *vrow = a.val ? a.val + (size_t)r * a.k : nullptr;
+  for (int i = (int)th.kk + tid; i < a.k; i += NT) {
+    irow[i] = -1;
+    if (vrow) vrow[i] = -INFINITY;
+  }
+  if (th.kk == 0) return;  // uniform
+  const bool keep = th.eq <= (uint32_t)kSelCap;
+  if (tid == 0) {
+    cnt64 = 0;
+    ctr[0] = th.above;
+  }
+  __syncthreads();
+  // pass 2: emit the columns above b1, collect the columns equal to b1
+  auto emit_round = [&](int base, const float (&sv)[U][4]) {
+    uint32_t fs = 0, fc = 0;  // this thread's 16 columns: above b1 / equal to b1
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = base + u * NT * 4 + 4 * tid + e;
+        const bool valid = valid_col(c);
+        const int dg = (int)(order_key(sv[u][e]) >> kHistShift);
+        fs |= (valid && dg > th.b1 ? 1u : 0u) << (u * 4 + e);
+        fc |= (valid && keep && dg == th.b1 ? 1u : 0u) << (u * 4 + e);
+      }
+    }
+    // positions: a wave-wide scan of the packed counts and one 64-bit LDS
+    // atomic per wave (at most 1024 of each kind per wave and round)
+    const uint32_t mine = ((uint32_t)__popc(fs) << 16) | (uint32_t)__popc(fc);
+    uint32_t incl = mine;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o, kWave);
+      if (lane_id() >= o) incl += y;
+    }
+    const uint32_t wtot = __shfl(incl, kWave - 1, kWave);
+    uint64_t wbase = 0;
+    if (lane_id() == 0 && wtot)
+      wbase = atomicAdd(&cnt64, ((uint64_t)(wtot >> 16) << 32) | (uint64_t)(wtot & 0xFFFFu));
+    wbase = ((uint64_t)__shfl((uint32_t)(wbase >> 32), 0, kWave) << 32) |
+            (uint64_t)__shfl((uint32_t)wbase, 0, kWave);
+    const uint32_t excl = incl - mine;
+    uint32_t so = (uint32_t)(wbase >> 32) + (excl >> 16);
+    uint32_t co = (uint32_t)wbase + (excl & 0xFFFFu);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int bit = u * 4 + e;
+        const int c = base + u * NT * 4 + 4 * tid + e;
+        if ((fs >> bit) & 1u) {
+          if (so < th.above) {
+            irow[so] = MAP ? mrow[c] : c;
+            if (vrow) vrow[so] = sv[u][e];
+          }
+          ++so;
+        }
+        if ((fc >> bit) & 1u) {
+          if (co < (uint32_t)kSelCap) cs[co] = composite(order_key(sv[u][e]), MAP ? mrow[c] : c);
+          ++co;
+        }
+      }
+    }
+  };
+  if (REG) {
+#pragma unroll
+    for (int rr = 0; rr < RR; ++rr)
+      if (rr * kSelRound < n) emit_round(rr * kSelRound, sv[rr]);
+  } else {
+    for (int base = 0; base < n; base += kSelRound) {
+      load_round(base, sv[0]);
+      emit_round(base, sv[0]);
+    }
+  }
+  __syncthreads();
+  resolve_candidates<MAP, NT>(cs, keep ? (int)th.eq : 0, keep, n, srow, mrow, th, irow, vrow, cs,
+                              cs2, hs, sh, ctr, res);
+}
+
 // -------------------------------------------------------------------- fill
 __global__ void fill_u32_kernel(uint32_t *p, size_t n, uint32_t v) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -314,6 +494,22 @@ hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t st) {
 hipError_t launch_topk_hist(const TopkArgs &a, uint32_t *hist, hipStream_t st) {
   dim3 grid((a.ld + a.chunk - 1) / a.chunk, a.rows);
   hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(256), 0, st, a, hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_rowselect(const TopkArgs &a, hipStream_t st) {
+  const bool reg = a.ld <= kRegCols;
+  if (a.map) {
+    if (reg)
+      hipLaunchKernelGGL((topk_rowselect_kernel<true, true>), dim3(a.rows), dim3(kSelThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((topk_rowselect_kernel<true, false>), dim3(a.rows), dim3(kSelThreads), 0, st, a);
+  } else {
+    if (reg)
+      hipLaunchKernelGGL((topk_rowselect_kernel<false, true>), dim3(a.rows), dim3(kSelThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((topk_rowselect_kernel<false, false>), dim3(a.rows), dim3(kSelThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 

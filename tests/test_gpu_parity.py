@@ -127,6 +127,28 @@ def test_topk_exact(kind, rows, ld, k):
         assert np.all(idx[r][idx[r] >= 0] < n)
 
 
+@pytest.mark.parametrize("k", [1, 200, 3000])
+def test_topk_exact_row_mode(k):
+    """Enough rows to fill the GPU take the one-workgroup-per-row select;
+    rows mix ties, all-equal (more tied candidates than fit in LDS), wide
+    dynamic range, short and empty prefixes."""
+    abi = _abi()
+    rows, ld = 300, 20000
+    rng = np.random.default_rng(k)
+    kinds = ["equal", "ties", "normal", "spread"]
+    v = np.stack([_topk_rows(rng, 1, ld, kinds[r % 4])[0] for r in range(rows)])
+    row_len = rng.integers(0, ld + 1, size=rows).astype(np.int32)
+    row_len[:8] = ld
+    row_len[8] = 0
+    row_len[9] = min(ld, k // 2)
+    idx, val = abi.topk(torch.from_numpy(v).cuda(), torch.from_numpy(row_len).cuda(), k)
+    idx, val = np_(idx), np_(val)
+    for r in range(rows):
+        n = int(row_len[r])
+        parity.check_exact_topk(idx[r], val[r], v[r], n, k, orc.topk_f32)
+        assert np.all(idx[r][idx[r] >= 0] < n)
+
+
 # ---------------------------------------------------------- score + top-k
 @pytest.mark.parametrize("S,Lmax,T,H,seed", CASES)
 @pytest.mark.parametrize("k", [1, 64, 600])
