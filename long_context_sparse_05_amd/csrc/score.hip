@@ -16,7 +16,9 @@
 // are padded to 272 bytes, so the MFMA-layout reads (lane = key column,
 // lane group = 8-element slice of d) hit 16 distinct bank groups.  The
 // weighted ReLU and the head reduction run on the accumulators in registers
-// (four rows per lane, then two cross-lane adds).  The epilogue also builds a
+// (four rows per lane), then a reduce-scatter across the four lane groups
+// leaves each group the whole sums of one tile, so a wave stores the scores
+// of 64 (or 32) consecutive columns at once.  The epilogue also builds a
 // 4096-bin histogram of the top 12 bits of each score's order key, the first
 // radix digit of the per-row top-k.
 #include "common.hpp"
@@ -30,9 +32,11 @@ template <int HT, bool GATHER, int U>
 __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
   __shared__ uint32_t lds_hist[kHistBins];
   __shared__ uint4 tile[4][16 * kKeyRowLds / 16];
+  __shared__ int32_t ctok[GATHER ? kMaxScoreChunk : 1];  // the chunk's candidate tokens
   const int t = blockIdx.y;
   const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform, and known to be: the step loop below branches on scalars
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;   // MFMA column (key) / 16-byte slice of a key row
   const int grp = lane >> 4;   // lane group: k sub-slice / accumulator rows / key of a load
   const bool hist = a.hist != nullptr;
@@ -79,25 +83,35 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
       wv[ht][r] = wr;
     }
   }
-  if (hist) __syncthreads();
-
   const int32_t *crow = GATHER ? a.cand + (size_t)t * a.ncols : nullptr;
+  if (GATHER)
+    for (int c = c0 + threadIdx.x; c < c1; c += 256) ctok[c - c0] = crow[c];
+  if (hist || GATHER) __syncthreads();
+
   char *wt = (char *)tile[wave];
   // U tiles of 16 keys per step; load i of tile u covers keys 4i..4i+3
+  // Every load is issued unconditionally, from a column clamped into
+  // [c0, c1) (and token 0 for an empty candidate slot): a load under a
+  // branch leaves the compiler unable to count the loads in flight, and it
+  // then waits for all of them -- the next step's included -- before each
+  // step.  The epilogue masks the columns that are not valid.
   auto load_step = [&](int base, uint4 (&kv)[U][4]) {
+    int tok[U][4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int c = base + u * 16 + 4 * i + grp;
-        int tok = -1;
-        if (c < c1 && c < nvalid) tok = GATHER ? crow[c] : c;
-        kv[u][i] = tok >= 0 ? load_nt16(a.keys + (seq_base + (size_t)tok) * kD + col * 8)
-                            : make_uint4(0, 0, 0, 0);
+        const int c = min(base + u * 16 + 4 * i + grp, c1 - 1);
+        tok[u][i] = GATHER ? max(ctok[c - c0], 0) : c;
       }
-    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        kv[u][i] = load_nt16(a.keys + (seq_base + (size_t)tok[u][i]) * kD + col * 8);
   };
   auto process_step = [&](int base, const uint4 (&kv)[U][4]) {
+    float part[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       // transpose through LDS: row = key within the tile, 16-byte slices
@@ -106,38 +120,68 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
       uint4 kb[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) kb[s] = *(const uint4 *)(wt + col * kKeyRowLds + (4 * s + grp) * 16);
-      float part = 0.f;
+      part[u] = 0.f;
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) acc = mfma16(qa[ht][s], as_bf16x8(kb[s]), acc);
+        // ReLU as a signed-integer max of the bits (-0 and negatives -> +0)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part += wv[ht][r] * fmaxf(acc[r], 0.f);
+        for (int r = 0; r < 4; ++r)
+          part[u] += wv[ht][r] * __int_as_float(max(__float_as_int(acc[r]), 0));
       }
-      part += __shfl_xor(part, 16, kWave);
-      part += __shfl_xor(part, 32, kWave);
-      const int c = base + u * 16 + col;
-      if (grp == 0 && c < c1) {
-        const bool ok = c < nvalid && (!GATHER || crow[c] >= 0);
-        const float sc = ok ? part : -INFINITY;
-        srow[c] = sc;
-        if (hist && ok) atomicAdd(&lds_hist[order_key(sc) >> kHistShift], 1u);
-      }
+    }
+    // reduce-scatter over the four lane groups (each holds four head rows):
+    // afterwards group g holds the whole sum of tile g (U == 4) or of tile
+    // g / 2 (U == 2), so one store covers U * 16 consecutive columns
+    float own;
+    if constexpr (U == 4) {
+      const bool lo = grp < 2;
+      const float x0 = (lo ? part[0] : part[2]) + __shfl_xor(lo ? part[2] : part[0], 32, kWave);
+      const float x1 = (lo ? part[1] : part[3]) + __shfl_xor(lo ? part[3] : part[1], 32, kWave);
+      const bool ev = (grp & 1) == 0;
+      own = (ev ? x0 : x1) + __shfl_xor(ev ? x1 : x0, 16, kWave);
+    } else {
+      static_assert(U == 2, "two or four tiles per step");
+      const bool lo = grp < 2;
+      own = (lo ? part[0] : part[1]) + __shfl_xor(lo ? part[1] : part[0], 32, kWave);
+      own += __shfl_xor(own, 16, kWave);
+    }
+    const int c = base + (U == 4 ? grp : grp >> 1) * 16 + col;
+    if ((U == 4 || (grp & 1) == 0) && c < c1) {
+      const bool ok = c < nvalid && (!GATHER || ctok[c - c0] >= 0);
+      const float sc = ok ? own : -INFINITY;
+      srow[c] = sc;
+      if (hist && ok) atomicAdd(&lds_hist[order_key(sc) >> kHistShift], 1u);
     }
   };
   // software pipeline over two register buffers: the next step's loads are
-  // in flight while the current step is transposed, contracted and stored
+  // in flight while the current step is transposed, contracted and stored.
+  // Every path that goes on has issued the next step's loads (the last
+  // steps leave the loop), so the compiler waits only for the step it
+  // processes.
   const int stride = 4 * 16 * U;
+  const int wstart = c0 + wave * 16 * U;
+  const int nsteps = wstart < c1 ? (c1 - wstart + stride - 1) / stride : 0;
   uint4 ka[U][4], kb2[U][4];
-  int base = c0 + wave * 16 * U;
-  if (base < c1) load_step(base, ka);
-  for (; base < c1; base += 2 * stride) {
-    if (base + stride < c1) load_step(base + stride, kb2);
-    process_step(base, ka);
-    if (base + stride >= c1) break;
-    if (base + 2 * stride < c1) load_step(base + 2 * stride, ka);
-    process_step(base + stride, kb2);
+  if (nsteps > 0) {
+    load_step(wstart, ka);
+    for (int st = 0;; st += 2) {
+      const int b0 = wstart + st * stride;
+      if (st + 1 >= nsteps) {
+        process_step(b0, ka);
+        break;
+      }
+      load_step(b0 + stride, kb2);
+      process_step(b0, ka);
+      if (st + 2 >= nsteps) {
+        process_step(b0 + stride, kb2);
+        break;
+      }
+      load_step(b0 + 2 * stride, ka);
+      process_step(b0 + stride, kb2);
+    }
   }
   if (hist) {
     __syncthreads();
@@ -152,7 +196,11 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
 template <int HT, bool GATHER>
 static hipError_t launch_ht(const ScoreArgs &a, hipStream_t st) {
   dim3 grid((a.ncols + a.chunk - 1) / a.chunk, a.T);
-  hipLaunchKernelGGL((score_rows_kernel<HT, GATHER, 2>), grid, dim3(256), 0, st, a);
+  // four 16-key tiles per step (one coalesced 256-byte score store per
+  // wave) where the query fragments leave room in registers, else two
+  constexpr int U = HT <= 2 ? 4 : 2;
+  if (GATHER && a.chunk > kMaxScoreChunk) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((score_rows_kernel<HT, GATHER, U>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

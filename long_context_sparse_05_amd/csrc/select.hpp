@@ -32,12 +32,7 @@ template <int NT>
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t *sh, uint32_t &total) {
   constexpr int NW = NT / kWave;
   const int lane = lane_id(), wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const uint32_t y = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += y;
-  }
+  const uint32_t incl = wave_incl_scan(v);
   if (lane == kWave - 1) sh[wave] = incl;
   __syncthreads();
   uint32_t base = 0;

@@ -44,7 +44,7 @@ __device__ __forceinline__ bool lds_append(bool pred, uint32_t *counter, uint32_
   const int leader = __ffsll((unsigned long long)m) - 1;
   uint32_t base = 0;
   if (lane_id() == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
-  base = __shfl(base, leader, kWave);
+  base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
   pos = base + lanes_below(m);
   return pred;
 }
@@ -188,11 +188,17 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a) {
 // output slots, starting at ctr[0]) and compacting the survivors, until the
 // crossing bin holds exactly the keys still needed.  Candidates come from
 // `cur` (keep) or are re-read from the score row (more than fit in LDS).
+//
+// The candidates are those whose composite key matches (prefix0, mask0); the
+// first pass takes the 8-bit digit at shift0 and later passes the digits
+// below it.  Candidates held in LDS may carry keys relative to key_base
+// (the emitted score is key_to_float(key + key_base)).
 template <bool MAP, int NT>
 __device__ __forceinline__ void resolve_candidates(
     uint64_t *cur, int ncur, bool keep, int n, const float *srow, const int32_t *mrow,
     const Thresh th, int32_t *irow, float *vrow, uint64_t *cs, uint64_t *cs2, uint32_t *hs,
-    uint32_t *sh, uint32_t *ctr, uint32_t *res) {
+    uint32_t *sh, uint32_t *ctr, uint32_t *res, uint64_t prefix0, uint64_t mask0, int shift0,
+    uint32_t key_base) {
   const int tid = threadIdx.x;
   // Visit every candidate that matches (prefix, mask) in uniform rounds of NT
   // (wave ballots stay legal): from LDS, or (too many ties) from the row.
@@ -221,15 +227,15 @@ __device__ __forceinline__ void resolve_candidates(
     uint32_t pos;
     if (lds_append(pred, &ctr[0], pos) && pos < th.kk) {
       irow[pos] = (int32_t)(~(uint32_t)ck);
-      if (vrow) vrow[pos] = key_to_float((uint32_t)(ck >> 32));
+      if (vrow) vrow[pos] = key_to_float((uint32_t)(ck >> 32) + key_base);
     }
   };
 
   uint32_t need = th.kk - th.above;
-  uint64_t prefix = (uint64_t)(uint32_t)th.b1 << 52;
-  uint64_t mask = 0xFFFull << 52;
-  for (int pass = 0; pass < 7; ++pass) {
-    const int shift = pass < 6 ? 44 - 8 * pass : 0;
+  uint64_t prefix = prefix0;
+  uint64_t mask = mask0;
+  for (int pass = 0;; ++pass) {
+    const int shift = max(shift0 - 8 * pass, 0);
     if (tid < 256) hs[tid] = 0;
     __syncthreads();
     for_each(prefix, mask, [&](bool ok, uint64_t ck) {
@@ -253,7 +259,7 @@ __device__ __forceinline__ void resolve_candidates(
     need -= above_d;
     prefix |= (uint64_t)d << shift;
     mask |= 0xFFull << shift;
-    if (cnt_d == need || pass == 6) {
+    if (cnt_d == need || shift == 0) {
       for_each(prefix, mask, [&](bool ok, uint64_t ck) { emit(ok, ck); });
       break;
     }
@@ -317,7 +323,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_finish_kernel(TopkArgs a) {
   if (tid == 0) ctr[0] = th.above;
   __syncthreads();
 
-  resolve_candidates<MAP, NT>(cs, ncur, keep, n, srow, mrow, th, irow, vrow, cs, cs2, hs, sh, ctr, res);
+  resolve_candidates<MAP, NT>(cs, ncur, keep, n, srow, mrow, th, irow, vrow, cs, cs2, hs, sh, ctr, res,
+                              (uint64_t)(uint32_t)th.b1 << 52, 0xFFFull << 52, 44, 0u);
 }
 
 // --------------------------------------------------------------- row select
@@ -325,13 +332,213 @@ __global__ __launch_bounds__(kSelThreads) void topk_finish_kernel(TopkArgs a) {
 // the whole selection: pass 1 builds the row's first-digit histogram in LDS,
 // pass 2 writes the columns above the threshold digit and collects the
 // digit's candidates in LDS, and the candidates are resolved.  No global
-// atomics and no zeroed workspace.  Rows of at most kRegCols columns (REG)
-// are read from HBM once: each thread keeps its 64 scores in registers from
-// pass 1 to pass 2.  Longer rows are streamed twice.
+// atomics and no zeroed workspace.  Rows of at most kRegCols columns with
+// ld % 4 == 0 (REG) are read from HBM once: each thread keeps its 64 scores
+// in registers from pass 1 to pass 2 (and the sample threshold first tries
+// to skip the histogram).  Other rows are streamed twice.
 constexpr int kSelU = 4;                                    // float4 loads per thread per round
 constexpr int kSelRound = kSelThreads * 4 * kSelU;          // columns per round
 constexpr int kRegRounds = 4;
 constexpr int kRegCols = kSelRound * kRegRounds;            // 65536
+
+// Sample threshold for a register-resident row of n columns (every column
+// valid) when k is a small fraction of n.  One score per thread -- 16
+// windows of 256 columns spread over the row -- gives an estimate tau of a
+// key a little below the k-th largest (a two-level 12-bit radix select of the
+// sample at rank ~ 1.25 k ns / n plus a margin).  One pass over the
+// registers collects the columns whose scores are >= tau (one compare
+// each); when there are at least k of them and no thread holds more than
+// 15, their keys relative to tau are ranked: a 12-bit digit histogram emits
+// every key above the k-th key's digit and the 8-bit passes resolve that
+// digit.  Otherwise nothing has been written and the caller runs the exact
+// histogram path.  Returns true when done.
+constexpr int kSampleMinCols = 8192;
+
+__device__ __forceinline__ bool sample_collect(const TopkArgs &a, int n,
+                                               const float (&sv)[kRegRounds][kSelU][4],
+                                               uint64_t *cs, uint32_t *sh, uint32_t &cnt_out,
+                                               uint32_t &tau_out, uint32_t &kk_out) {
+  constexpr int NT = kSelThreads;
+  constexpr int NW = NT / kWave;
+  static_assert(NW == kRegRounds * kSelU, "one sample window per wave");
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const uint32_t kk = (uint32_t)min(a.k, n);
+  if (n < kSampleMinCols || kk * 8u > (uint32_t)n) return false;
+  uint32_t *lh = (uint32_t *)cs;
+  uint32_t *res = sh + NW + 4;
+
+  // the sample: wave w takes element 0 of its (round, group) w
+  float smp = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i)
+    if (wave == i) smp = sv[i / kSelU][i % kSelU][0];
+  const int scol = (wave / kSelU) * kSelRound + (wave % kSelU) * NT * 4 + 4 * tid;
+  const bool sok = scol < n;
+  const uint32_t skey = order_key(smp);
+
+  for (int i = tid; i < kHistBins; i += NT) lh[i] = 0;
+  __syncthreads();
+  if (sok) atomicAdd(&lh[skey >> kHistShift], 1u);
+  // block-wide values read back from LDS are uniform: readfirstlane lets the
+  // compiler see that, so the early exits are scalar branches and the row's
+  // registers are not kept live through the resolve below
+  const int ns = __builtin_amdgcn_readfirstlane(__syncthreads_count(sok));
+  const float m = (float)kk * (float)ns / (float)n;
+  const int rs = (int)ceilf(1.25f * m + 3.f * sqrtf(m) + 4.f);
+  if (rs >= ns) return false;  // uniform; the histogram is rebuilt by the caller
+  Thresh t1 = threshold_from_lds<NT>(lh, (uint32_t)rs, sh);
+  t1.b1 = __builtin_amdgcn_readfirstlane(t1.b1);
+  t1.above = __builtin_amdgcn_readfirstlane(t1.above);
+  for (int i = tid; i < kHistBins; i += NT) lh[i] = 0;
+  if (tid == 0) {
+    res[3] = 0;  // candidates
+    res[4] = 0;  // a thread ran out of slots
+    res[5] = 0;  // largest relative key
+  }
+  __syncthreads();
+  if (sok && (int)(skey >> kHistShift) == t1.b1) atomicAdd(&lh[(skey >> 8) & 0xFFFu], 1u);
+  __syncthreads();
+  const Thresh t2 = threshold_from_lds<NT>(lh, (uint32_t)rs - t1.above, sh);
+  const uint32_t b2 = __builtin_amdgcn_readfirstlane(t2.b1);
+  const uint32_t tau = ((uint32_t)t1.b1 << kHistShift) | (b2 << 8);
+  // tau must name a normal float or an infinity: then "score >= tf" agrees
+  // with "order_key(score) >= tau" whatever the denormal mode
+  if (tau < 0x00800000u || tau > 0xFF800000u || (tau >= 0x7F800000u && tau <= 0x807FFFFFu))
+    return false;
+  const float tf = key_to_float(tau);
+
+  // one branch-free pass: each thread appends the columns with score >= tf
+  // to its own slots (slot j of thread t at j*NT + t, so a wave's stores hit
+  // consecutive words whatever its lanes' counts); a column below tf is
+  // written to the next free slot and overwritten by the next hit.  A thread
+  // keeps at most SLOTS - 1 hits (the last slot is the scratch).
+  constexpr int SLOTS = kSelCap / NT;
+  uint32_t *cv = (uint32_t *)cs;  // scores
+  uint32_t *cc = cv + kSelCap;    // columns
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int rr = 0; rr < kRegRounds; ++rr) {
+    const int base = rr * kSelRound;
+    if (base < n) {
+      const bool all = base + kSelRound <= n;
+#pragma unroll
+      for (int u = 0; u < kSelU; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = base + u * NT * 4 + 4 * tid + e;
+          const uint32_t at = min(cnt, (uint32_t)SLOTS - 1) * NT + tid;
+          cv[at] = __float_as_uint(sv[rr][u][e]);
+          cc[at] = (uint32_t)c;
+          cnt += ((all || c < n) && sv[rr][u][e] >= tf) ? 1u : 0u;
+        }
+    }
+  }
+  const uint32_t wsum = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(cnt), kWave - 1);
+  const bool wover = __ballot(cnt >= (uint32_t)SLOTS) != 0;
+  if (lane_id() == 0) {
+    atomicAdd(&res[3], wsum);
+    if (wover) atomicOr(&res[4], 1u);
+  }
+  __syncthreads();
+  const uint32_t total = __builtin_amdgcn_readfirstlane(res[3]);
+  if (__builtin_amdgcn_readfirstlane(res[4]) || total < kk) return false;
+  cnt_out = cnt;
+  tau_out = tau;
+  kk_out = kk;
+  return true;
+}
+
+// The ranking of the candidates sample_collect left in LDS (thread t's
+// slots j < cnt at j*NT + t).  The row's registers are dead here: this is
+// entered only when the collection succeeded, and the kernel ends after it.
+__device__ __forceinline__ void sample_finish(const TopkArgs &a, int n, uint32_t kk, uint32_t tau,
+                                              uint32_t cnt, uint64_t *cs, uint64_t *cs2,
+                                              uint32_t *hs, uint32_t *sh) {
+  constexpr int NT = kSelThreads;
+  constexpr int NW = NT / kWave;
+  constexpr int SLOTS = kSelCap / NT;
+  const int tid = threadIdx.x;
+  uint32_t *lh = (uint32_t *)cs;
+  uint32_t *ctr = sh + NW;
+  uint32_t *res = sh + NW + 4;
+  const uint32_t *cv = (const uint32_t *)cs;
+  const uint32_t *cc = cv + kSelCap;
+
+  // the candidates' keys relative to tau and their columns stay in
+  // registers (two 32-bit arrays, every element written: a conditionally
+  // written 64-bit array is kept as one vector and copied whole)
+  uint32_t rk[SLOTS - 1], col[SLOTS - 1];
+  uint32_t kmax = 0;
+#pragma unroll
+  for (int jj = 0; jj < SLOTS - 1; ++jj) {
+    const bool ok = jj < (int)cnt;
+    const uint32_t at = ok ? jj * NT + tid : tid;
+    const uint32_t rel = order_key(__uint_as_float(cv[at])) - tau;
+    rk[jj] = rel;
+    col[jj] = cc[at];
+    kmax = ok ? max(kmax, rel) : kmax;
+  }
+  kmax = wave_max_u32(kmax);
+  if (lane_id() == 0 && kmax) atomicMax(&res[5], kmax);
+  int32_t *irow = a.idx + (size_t)blockIdx.x * a.k;
+  float *vrow = a.val ? a.val + (size_t)blockIdx.x * a.k : nullptr;
+  for (int i = (int)kk + tid; i < a.k; i += NT) {
+    irow[i] = -1;
+    if (vrow) vrow[i] = -INFINITY;
+  }
+  __syncthreads();  // every slot read: the LDS is free for the histogram
+  const uint32_t top = __builtin_amdgcn_readfirstlane(res[5]);
+  const int bits = top ? 32 - __clz(top) : 0;  // relative keys fit in `bits` bits
+  const int dshift = max(bits - kHistBits, 0);
+
+  // 12-bit digit of the relative key: emit the keys above the digit of the
+  // kk-th key, then resolve that digit's keys
+  for (int i = tid; i < kHistBins; i += NT) lh[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int jj = 0; jj < SLOTS - 1; ++jj)
+    if (jj < (int)cnt) atomicAdd(&lh[rk[jj] >> dshift], 1u);
+  __syncthreads();
+  Thresh th = threshold_from_lds<NT>(lh, kk, sh);
+  th.b1 = __builtin_amdgcn_readfirstlane(th.b1);
+  th.above = __builtin_amdgcn_readfirstlane(th.above);
+  th.eq = __builtin_amdgcn_readfirstlane(th.eq);
+  const bool take_eq = th.eq == kk - th.above;  // the digit holds exactly the keys still needed
+  // positions from one block scan of packed per-thread counts (at most 15
+  // each, 15360 in all): emitted keys (digit above b1, or b1 itself when it
+  // holds exactly the keys still needed) high, the digit's keys to resolve low
+  uint32_t ne = 0, nq = 0;
+#pragma unroll
+  for (int jj = 0; jj < SLOTS - 1; ++jj) {
+    const bool ok = jj < (int)cnt;
+    const int dg = (int)(rk[jj] >> dshift);
+    ne += (ok && (dg > th.b1 || (take_eq && dg == th.b1))) ? 1u : 0u;
+    nq += (ok && !take_eq && dg == th.b1) ? 1u : 0u;
+  }
+  const uint32_t mine = (ne << 16) | nq;
+  uint32_t tot;
+  const uint32_t excl = block_scan<NT>(mine, sh, tot) - mine;
+  uint32_t pe = excl >> 16, pq = excl & 0xFFFFu;
+  uint64_t *eqk = cs;  // every slot has been read: the words are free
+#pragma unroll
+  for (int jj = 0; jj < SLOTS - 1; ++jj) {
+    const bool ok = jj < (int)cnt;
+    const int dg = (int)(rk[jj] >> dshift);
+    if (ok && (dg > th.b1 || (take_eq && dg == th.b1))) {
+      if (pe < kk) {
+        irow[pe] = (int32_t)col[jj];
+        if (vrow) vrow[pe] = key_to_float(rk[jj] + tau);
+      }
+      ++pe;
+    }
+    if (ok && !take_eq && dg == th.b1) eqk[pq++] = composite(rk[jj], (int)col[jj]);
+  }
+  if (take_eq) return;  // uniform
+  if (tid == 0) ctr[0] = th.above;  // next output slot
+  __syncthreads();
+  resolve_candidates<false, NT>(eqk, (int)th.eq, true, n, nullptr, nullptr, th, irow, vrow, cs, cs2,
+                                hs, sh, ctr, res, 0ull, 0ull, max(32 + dshift - 8, 0), tau);
+}
 
 template <bool MAP, bool REG>
 __global__ __launch_bounds__(kSelThreads) void topk_rowselect_kernel(TopkArgs a) {
@@ -378,13 +585,32 @@ __global__ __launch_bounds__(kSelThreads) void topk_rowselect_kernel(TopkArgs a)
           atomicAdd(&lh[order_key(sv[u][e]) >> kHistShift], 1u);
   };
 
-  for (int i = tid; i < kHistBins; i += NT) lh[i] = 0;
-  __syncthreads();
   float sv[RR][U][4];
-  if (REG) {  // pass 1: every load of the row in flight, then the histogram
+  if constexpr (REG) {
+    // every load of the row in flight at once: float4 loads with the column
+    // clamped into the row (ld % 4 == 0, so a float4 at c < ld stays inside
+    // it); columns at or past n hold stale values that every use masks out
 #pragma unroll
     for (int rr = 0; rr < RR; ++rr)
-      if (rr * kSelRound < n) load_round(rr * kSelRound, sv[rr]);
+      if (rr * kSelRound < n) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t cf = (uint32_t)min(rr * kSelRound + u * NT * 4 + 4 * tid, a.ld - 4);
+          const float4 x = *(const float4 *)((const char *)srow + cf * 4u);
+          sv[rr][u][0] = x.x; sv[rr][u][1] = x.y; sv[rr][u][2] = x.z; sv[rr][u][3] = x.w;
+        }
+      }
+    if constexpr (!MAP) {
+      uint32_t cnt, tau, kk;
+      if (sample_collect(a, n, sv, cs, sh, cnt, tau, kk)) {  // uniform
+        sample_finish(a, n, kk, tau, cnt, cs, cs2, hs, sh);
+        return;
+      }
+    }
+  }
+  for (int i = tid; i < kHistBins; i += NT) lh[i] = 0;
+  __syncthreads();
+  if (REG) {  // pass 1: the histogram of the registers
 #pragma unroll
     for (int rr = 0; rr < RR; ++rr)
       if (rr * kSelRound < n) hist_round(rr * kSelRound, sv[rr]);
@@ -426,18 +652,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_rowselect_kernel(TopkArgs a)
     // positions: a wave-wide scan of the packed counts and one 64-bit LDS
     // atomic per wave (at most 1024 of each kind per wave and round)
     const uint32_t mine = ((uint32_t)__popc(fs) << 16) | (uint32_t)__popc(fc);
-    uint32_t incl = mine;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const uint32_t y = __shfl_up(incl, o, kWave);
-      if (lane_id() >= o) incl += y;
-    }
-    const uint32_t wtot = __shfl(incl, kWave - 1, kWave);
+    const uint32_t incl = wave_incl_scan(mine);
+    const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
     uint64_t wbase = 0;
     if (lane_id() == 0 && wtot)
       wbase = atomicAdd(&cnt64, ((uint64_t)(wtot >> 16) << 32) | (uint64_t)(wtot & 0xFFFFu));
-    wbase = ((uint64_t)__shfl((uint32_t)(wbase >> 32), 0, kWave) << 32) |
-            (uint64_t)__shfl((uint32_t)wbase, 0, kWave);
+    wbase = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(wbase >> 32), 0) << 32) |
+            (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)wbase, 0);
     const uint32_t excl = incl - mine;
     uint32_t so = (uint32_t)(wbase >> 32) + (excl >> 16);
     uint32_t co = (uint32_t)wbase + (excl & 0xFFFFu);
@@ -473,7 +694,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_rowselect_kernel(TopkArgs a)
   }
   __syncthreads();
   resolve_candidates<MAP, NT>(cs, keep ? (int)th.eq : 0, keep, n, srow, mrow, th, irow, vrow, cs,
-                              cs2, hs, sh, ctr, res);
+                              cs2, hs, sh, ctr, res, (uint64_t)(uint32_t)th.b1 << 52, 0xFFFull << 52,
+                              44, 0u);
 }
 
 // -------------------------------------------------------------------- fill
@@ -498,7 +720,7 @@ hipError_t launch_topk_hist(const TopkArgs &a, uint32_t *hist, hipStream_t st) {
 }
 
 hipError_t launch_topk_rowselect(const TopkArgs &a, hipStream_t st) {
-  const bool reg = a.ld <= kRegCols;
+  const bool reg = a.ld <= kRegCols && a.ld % 4 == 0;
   if (a.map) {
     if (reg)
       hipLaunchKernelGGL((topk_rowselect_kernel<true, true>), dim3(a.rows), dim3(kSelThreads), 0, st, a);

@@ -149,6 +149,49 @@ def test_topk_exact_row_mode(k):
         assert np.all(idx[r][idx[r] >= 0] < n)
 
 
+def _skewed_rows(rng, rows, ld, kind):
+    """Rows whose columns = 0 mod 4 differ from the rest, so that an estimate
+    drawn from such columns misjudges the k-th score (both ways), plus
+    needles and a ramp along the row."""
+    v = rng.standard_normal((rows, ld)).astype(np.float32)
+    c = np.arange(ld)
+    if kind == "mod4_hi":
+        v[:, c % 4 == 0] += 6.0
+    elif kind == "mod4_lo":
+        v[:, c % 4 == 0] -= 6.0
+    elif kind == "needles":
+        for r in range(rows):
+            v[r, rng.choice(ld, 40, replace=False)] = 50.0 + rng.standard_normal(40).astype(np.float32)
+    elif kind == "ramp":
+        v += (c / ld * 4.0).astype(np.float32)
+    elif kind == "ties":
+        v = np.round(v * 4.0) / 4.0
+    return v
+
+
+@pytest.mark.parametrize("ld,k", [(65536, 2048), (65536, 64), (8192, 1000), (65528, 700)])
+def test_topk_row_mode_long_rows(ld, k):
+    """One-workgroup-per-row select on long rows: the sampled threshold is
+    taken where it brackets the k-th score, and the exact histogram path
+    otherwise (too few or too many columns above the estimate)."""
+    abi = _abi()
+    rows = 256
+    rng = np.random.default_rng(ld + k)
+    kinds = ["normal", "mod4_hi", "mod4_lo", "needles", "ramp", "ties"]
+    v = np.concatenate([_skewed_rows(rng, (rows + 5) // 6, ld, kd) for kd in kinds])[:rows]
+    row_len = np.full(rows, ld, np.int32)
+    row_len[1::7] = rng.integers(k, ld + 1, size=len(row_len[1::7]))   # ragged prefixes
+    row_len[2] = ld - 1
+    row_len[3] = 8 * k - 3          # just below the sampled path's k <= n/8 bound
+    row_len[4] = min(ld, 8 * k)     # just at it
+    idx, val = abi.topk(torch.from_numpy(v).cuda(), torch.from_numpy(row_len).cuda(), k)
+    idx, val = np_(idx), np_(val)
+    for r in range(rows):
+        n = int(row_len[r])
+        parity.check_exact_topk(idx[r], val[r], v[r], n, k, orc.topk_f32)
+        assert np.all(idx[r][idx[r] >= 0] < n)
+
+
 # ---------------------------------------------------------- score + top-k
 @pytest.mark.parametrize("S,Lmax,T,H,seed", CASES)
 @pytest.mark.parametrize("k", [1, 64, 600])
