@@ -268,6 +268,19 @@ static RouteArgs make_route_args(const misa_batch *b, const float *pooled, int32
   return a;
 }
 
+// Many queries of one sequence (a prefill chunk) with at most 64 heads: the
+// tiled one-kernel router.  Otherwise the per-query partial + final pair,
+// whose final kernel also clears the selection histogram of the fused call.
+constexpr int kRouteTileMinRows = 64;
+hipError_t dispatch_route(const misa_batch *b, const RouteArgs &a, hipStream_t st, bool &zeroed) {
+  if (b->S == 1 && b->T >= kRouteTileMinRows && b->H <= 64) {
+    zeroed = false;
+    return launch_route_tile(a, st);
+  }
+  zeroed = a.zero_hist != nullptr;
+  return launch_route(a, st);
+}
+
 int misa_route(const misa_batch *b, const float *pooled, int32_t B, int32_t h, int32_t mode,
                int32_t *heads, float *head_score, void *ws, size_t ws_bytes, void *stream) {
   int rc = check_batch(b, true);
@@ -277,7 +290,8 @@ int misa_route(const misa_batch *b, const float *pooled, int32_t B, int32_t h, i
   if (mode != 0 && mode != 1) return MISA_ERR_SHAPE;
   if (ws_bytes < route_bytes(b, B)) return MISA_ERR_WORKSPACE;
   const RouteArgs a = make_route_args(b, pooled, B, h, mode, heads, head_score, ws);
-  return hip_status(launch_route(a, (hipStream_t)stream));
+  bool zeroed;
+  return hip_status(dispatch_route(b, a, (hipStream_t)stream, zeroed));
 }
 
 int misa_score(const misa_batch *b, const int32_t *heads, int32_t h, float *scores,
@@ -367,7 +381,8 @@ int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t
   RouteArgs ra = make_route_args(b, pooled, B, h, mode, heads, head_score, ws);
   ra.zero_hist = (uint32_t *)((char *)sws + L.hist);
   ra.zero_ctr = (uint32_t *)((char *)sws + L.counters);
-  if (launch_route(ra, (hipStream_t)stream) != hipSuccess) return MISA_ERR_HIP;
+  bool zeroed;
+  if (dispatch_route(b, ra, (hipStream_t)stream, zeroed) != hipSuccess) return MISA_ERR_HIP;
   if (use_prefill(b, heads, h)) {
     float *sc = (float *)((char *)sws + L.scores);
     if (ev_start && hipEventRecord((hipEvent_t)ev_start, (hipStream_t)stream) != hipSuccess)
@@ -377,7 +392,7 @@ int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t
     if (ev_stop && hipEventRecord((hipEvent_t)ev_stop, (hipStream_t)stream) != hipSuccess)
       return MISA_ERR_HIP;
     return run_select(nullptr, sc, b->T, b->Lmax, b->q_pos, 1, nullptr, k, idx, val, sws, L,
-                      (hipStream_t)stream, nullptr, nullptr, true);
+                      (hipStream_t)stream, nullptr, nullptr, zeroed);
   }
   ScoreArgs s = make_score_args(b, heads, h);
   s.scores = (float *)((char *)sws + L.scores);
@@ -386,7 +401,7 @@ int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t
   s.ld = b->Lmax;
   s.chunk = score_chunk(b->T, b->Lmax);
   return run_select(&s, nullptr, b->T, b->Lmax, b->q_pos, 1, nullptr, k, idx, val, sws, L,
-                    (hipStream_t)stream, ev_start, ev_stop, true);
+                    (hipStream_t)stream, ev_start, ev_stop, zeroed);
 }
 
 int misa_indexer(const misa_batch *b, const float *pooled, int32_t B, int32_t h, int32_t mode,

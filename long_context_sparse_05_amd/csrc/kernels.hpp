@@ -82,5 +82,7 @@ struct RouteArgs {
 };
 constexpr int kRouteChunk = 64;  // complete blocks per router workgroup
 hipError_t launch_route(const RouteArgs &a, hipStream_t st);
+// many queries of one sequence, H <= 64: one kernel, heads written directly
+hipError_t launch_route_tile(const RouteArgs &a, hipStream_t st);
 
 }  // namespace misa

@@ -248,6 +248,49 @@ def test_route(S, Lmax, T, H, seed, B, mode):
                     "router heads differ at margin %g" % parity.head_margin(og[t], h)
 
 
+ROUTE_TILE_CASES = [
+    # Lmax, T, H, B, positions, mode
+    (3000, 200, 32, 64, "tail", 0),
+    (1100, 97, 8, 16, "random", 1),
+    (2500, 130, 64, 128, "random", 0),
+    (700, 64, 16, 1, "tail", 0),
+    (4200, 256, 64, 128, "tail", 1),
+    (5000, 70, 32, 128, "early", 0),
+]
+
+
+@pytest.mark.parametrize("Lmax,T,H,B,positions,mode", ROUTE_TILE_CASES)
+def test_route_prefill_tiles(Lmax, T, H, B, positions, mode):
+    """Many queries of one sequence take the tiled one-kernel router: the
+    importances and the routed heads match the oracle, including queries
+    whose prefix is shorter than one block and prefixes ending on a block
+    boundary."""
+    abi = _abi()
+    rng = np.random.default_rng(Lmax + T + B)
+    if positions == "tail":
+        q_pos = np.arange(Lmax - T, Lmax, dtype=np.int32)
+    elif positions == "early":
+        q_pos = np.concatenate([np.arange(0, 40), rng.integers(0, Lmax, T - 42), [B - 1, 2 * B - 1]])
+        q_pos = q_pos.astype(np.int32)
+    else:
+        q_pos = np.sort(rng.integers(0, Lmax, size=T)).astype(np.int32)
+    case = synth.random_case(1, Lmax, T, H, seed=Lmax % 97, q_pos=q_pos, q_seq=np.zeros(T, np.int32))
+    b = upload(case)
+    ob = orc.Batch.from_case(case)
+    pooled = abi.pool(b, B)
+    for h in sorted({1, min(8, H), H}):
+        heads, g = abi.route(b, pooled, B, h, mode, want_score=True)
+        heads, g = np_(heads), np_(g)
+        oheads, og = orc.route(ob, B, h, mode)
+        for t in range(T):
+            sb = float(np.mean(np.abs(og[t])))
+            assert np.all(np.abs(g[t] - og[t]) <= 1e-4 * (np.abs(og[t]) + sb)), (t, g[t], og[t])
+            assert list(heads[t]) == list(orc.topk_f32(g[t], h)), t
+            if list(heads[t]) != list(oheads[t]):
+                assert parity.head_margin(og[t], h) < 1e-4 or sorted(heads[t]) == sorted(oheads[t]), \
+                    "router heads differ at margin %g" % parity.head_margin(og[t], h)
+
+
 # --------------------------------------------------------------------- rerank
 @pytest.mark.parametrize("S,Lmax,T,H,seed", CASES[:4])
 def test_rerank(S, Lmax, T, H, seed):
