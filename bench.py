@@ -281,6 +281,19 @@ def main(argv=None):
         ev.record(t_stop, sp)
         torch.cuda.synchronize()
         ms_sep = ev.ms(t_start, t_stop) / K
+    # cold caches: before each step a 1 GiB fill evicts L2 and the 256 MB
+    # MALL, and events bracket the step alone (reported beside the headline,
+    # which times back-to-back steps)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cev = [(ev.create(), ev.create()) for _ in range(K)]
+    for i in range(K):
+        flush.fill_(float(i))
+        ev.record(cev[i][0], sp)
+        step()
+        ev.record(cev[i][1], sp)
+    torch.cuda.synchronize()
+    cold_ms = float(np.mean([ev.ms(a, c) for a, c in cev]))
+    del flush
     step()  # leave the fused call's outputs for the parity check
     torch.cuda.synchronize()
 
@@ -319,6 +332,7 @@ def main(argv=None):
         "config": {"workload": args.workload, "sequences": int(b.S), "context": int(b.Lmax),
                    "queries": int(b.T), "H_I": int(b.H), "B": B, "h": h, "k": k, "d": 128},
         "us_per_batch": ms_step * 1e3,
+        "us_per_batch_cold": cold_ms * 1e3,
         "score_kernel_us": score_ms * 1e3,
         "wall_s_timed": wall,
         "roofline": roof,

@@ -121,6 +121,27 @@ int misa_workspace_bytes(const misa_batch *b, int32_t op, int32_t B, int32_t h,
 int misa_pool(const misa_batch *b, int32_t B, float *pooled, void *stream);
 
 /*
+ * misa_pool_append -- bring misa_pool's output up to date after keys were
+ * appended to the sequences (streaming decode), recomputing only the blocks
+ * that hold an appended key.  The router's block summaries are a cache
+ * computed once (Methodology: MISA, Lightweight Block-Pooled Router, whose
+ * cost is per-head affinities over the M pooled blocks); appending a token
+ * changes only block floor(L / B), so each decode step costs O(B d) here.
+ *   seq_lens  (in the batch) the lengths after the append.
+ *   old_lens  int32 [S] (device): the lengths pooled last reflects.
+ *   max_new   host: an upper bound of seq_lens[s] - old_lens[s] over s;
+ *             0 <= max_new <= Lmax.
+ *   pooled    fp32 [S][ceil(Lmax/B)][d], updated in place: blocks
+ *             floor(old_lens[s]/B) .. ceil(seq_lens[s]/B)-1 are rewritten
+ *             exactly as misa_pool writes them; the others are not touched.
+ * Device-resident values are not checked: 0 <= old_lens[s] <= seq_lens[s]
+ * <= Lmax and seq_lens[s] - old_lens[s] <= max_new are the caller's to
+ * keep (otherwise some appended blocks are left stale).
+ */
+int misa_pool_append(const misa_batch *b, int32_t B, const int32_t *old_lens, int32_t max_new,
+                     float *pooled, void *stream);
+
+/*
  * misa_route -- the block-pooled head router (Methodology: MISA,
  * Lightweight Block-Pooled Router; the MISA abstract's query-dependent
  * subset of heads).  For query t with b_t = floor(p_t / B):

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(HERE, "libmisa_indexer.so")
 MISA_OP_DENSE, MISA_OP_ROUTE, MISA_OP_SCORE_TOPK, MISA_OP_RERANK, MISA_OP_TOPK, MISA_OP_INDEXER = range(6)
 
 # Every entry point include/misa_indexer.h declares.
-EXPORTS = ("misa_workspace_bytes", "misa_pool", "misa_route", "misa_score", "misa_topk",
+EXPORTS = ("misa_workspace_bytes", "misa_pool", "misa_pool_append", "misa_route", "misa_score", "misa_topk",
            "misa_score_topk", "misa_score_topk_ev", "indexer_dense", "misa_rerank",
            "misa_indexer", "misa_indexer_ev", "misa_status_str")
 
@@ -168,6 +168,19 @@ def pool(batch: Batch, B: int, out=None, stream=None):
     _need(out, torch.float32, "pooled")
     _check(load().misa_pool(ctypes.byref(batch.c), B, _ptr(out), _stream(stream)), "misa_pool")
     return out
+
+
+def pool_append(batch: Batch, B: int, old_lens, max_new: int, pooled, stream=None):
+    """Bring `pooled` (misa_pool's output) up to date in place after keys were
+    appended: the batch's seq_lens hold the new lengths, old_lens (int32 [S] on
+    the device) the lengths pooled reflects, max_new bounds the keys appended
+    to any sequence.  Only the blocks that hold an appended key are rewritten."""
+    torch = _torch()
+    _need(pooled, torch.float32, "pooled")
+    _need(old_lens, torch.int32, "old_lens", 1)
+    _check(load().misa_pool_append(ctypes.byref(batch.c), B, _ptr(old_lens), int(max_new), _ptr(pooled),
+                                   _stream(stream)), "misa_pool_append")
+    return pooled
 
 
 def route(batch: Batch, pooled, B: int, h: int, mode: int = 0, heads=None, head_score=None,

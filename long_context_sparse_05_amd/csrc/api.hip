@@ -244,6 +244,17 @@ int misa_pool(const misa_batch *b, int32_t B, float *pooled, void *stream) {
                                 (hipStream_t)stream));
 }
 
+int misa_pool_append(const misa_batch *b, int32_t B, const int32_t *old_lens, int32_t max_new,
+                     float *pooled, void *stream) {
+  int rc = check_batch(b, false);
+  if (rc) return rc;
+  if (!b->seq_lens || !old_lens || !pooled) return MISA_ERR_NULL;
+  if (B < 1 || B > b->Lmax || max_new < 0 || max_new > b->Lmax) return MISA_ERR_SHAPE;
+  if (b->S > kMaxRows) return MISA_ERR_UNSUPPORTED;
+  return hip_status(launch_pool_append(b->keys, b->seq_lens, old_lens, max_new, b->S, b->Lmax, B,
+                                       pooled, (hipStream_t)stream));
+}
+
 static RouteArgs make_route_args(const misa_batch *b, const float *pooled, int32_t B, int32_t h,
                                  int32_t mode, int32_t *heads, float *head_score, void *ws) {
   RouteArgs a{};

@@ -64,6 +64,9 @@ hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t st);
 // Block mean-pool (pool.hip).
 hipError_t launch_pool(const uint16_t *keys, const int32_t *seq_lens, int S, int Lmax,
                        int B, float *pooled, hipStream_t st);
+hipError_t launch_pool_append(const uint16_t *keys, const int32_t *seq_lens,
+                              const int32_t *old_lens, int max_new, int S, int Lmax, int B,
+                              float *pooled, hipStream_t st);
 
 // Head router (route.hip).
 struct RouteArgs {

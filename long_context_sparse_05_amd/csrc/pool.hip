@@ -6,6 +6,11 @@
 // Block-Pooled Router).  pooled[s][b] = mean of keys[s][i] over the keys
 // present in [bB, bB+B); a block with none is zeros.
 //
+// misa_pool_append reuses the kernel for a streaming key cache: after keys
+// are appended only the blocks that now hold them change, so the cost per
+// decode step is O(B d) instead of a pass over the cache (the router's
+// per-query cost is then O(H_I M) with no pooling pass).
+//
 // One wave per block: each lane loads 16 bytes (8 bf16) of one of 4
 // consecutive keys per step, so a wave streams 1 KiB contiguous per load;
 // fp32 partial sums are combined across the 4 lane groups with two xor
@@ -13,17 +18,24 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+#include <algorithm>
+
 namespace misa {
 
+// With old_lens (an append), block b of sequence s counts from
+// floor(old_lens[s] / B), and blocks with no key present are left alone:
+// only the blocks that hold an appended key are recomputed.
 __global__ __launch_bounds__(256) void pool_kernel(const uint16_t *keys, const int32_t *seq_lens,
-                                                   int Lmax, int B, int Mmax, float *pooled) {
+                                                   const int32_t *old_lens, int Lmax, int B,
+                                                   int Mmax, float *pooled) {
   const int s = blockIdx.y;
-  const int b = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int b = (old_lens ? old_lens[s] / B : 0) + blockIdx.x * 4 + (threadIdx.x >> 6);
   if (b >= Mmax) return;  // wave-uniform; no barrier in this kernel
   const int lane = lane_id();
   const int g = lane >> 4, cc = lane & 15;
   const int lo = b * B;
   const int hi = min(lo + B, min(seq_lens[s], Lmax));
+  if (old_lens && lo >= hi) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const uint16_t *base = keys + (size_t)s * Lmax * kD + cc * 8;
   int i = lo + g;
@@ -75,7 +87,20 @@ hipError_t launch_pool(const uint16_t *keys, const int32_t *seq_lens, int S, int
                        float *pooled, hipStream_t st) {
   const int Mmax = (Lmax + B - 1) / B;
   dim3 grid((Mmax + 3) / 4, S);
-  hipLaunchKernelGGL(pool_kernel, grid, dim3(256), 0, st, keys, seq_lens, Lmax, B, Mmax, pooled);
+  hipLaunchKernelGGL(pool_kernel, grid, dim3(256), 0, st, keys, seq_lens, nullptr, Lmax, B, Mmax,
+                     pooled);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_append(const uint16_t *keys, const int32_t *seq_lens,
+                              const int32_t *old_lens, int max_new, int S, int Lmax, int B,
+                              float *pooled, hipStream_t st) {
+  const int Mmax = (Lmax + B - 1) / B;
+  // appending n keys touches at most ceil(n / B) + 1 blocks of a sequence
+  const int nb = std::min(Mmax, (max_new + B - 1) / B + 1);
+  dim3 grid((nb + 3) / 4, S);
+  hipLaunchKernelGGL(pool_kernel, grid, dim3(256), 0, st, keys, seq_lens, old_lens, Lmax, B, Mmax,
+                     pooled);
   return hipGetLastError();
 }
 

@@ -68,9 +68,10 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a) {
     atomicMin(&sh_pmin, p);
   }
   __syncthreads();
-  const int kend = min(k1, sh_pmax + 1);
+  // (read back through readfirstlane: the tile loops below branch on scalars)
+  const int kend = __builtin_amdgcn_readfirstlane(min(k1, sh_pmax + 1));
   const bool all_rows = qt0 + QWG <= a.T;
-  const int kfull = all_rows ? min(k1, sh_pmin + 1) : 0;  // [k0, kfull): no mask
+  const int kfull = __builtin_amdgcn_readfirstlane(all_rows ? min(k1, sh_pmin + 1) : 0);
 
   // A fragments: row l32 of tile rt holds (query, head slot) of the layout above
   bf16x8 qa[RT][8];
@@ -111,46 +112,53 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a) {
     }
   }
 
-  // coalesced tile load: thread = (key lane tid/16, 16-byte slice tid%16)
+  // coalesced tile load: thread = (key lane tid/16, 16-byte slice tid%16).
+  // Every load is issued, from a key clamped below kend (the epilogue masks
+  // those keys), and the next tile is always prefetched (the last one again
+  // at the end): loads under branches leave the compiler unable to count the
+  // memory operations in flight, and it then waits for all of them -- the
+  // previous tile's score stores included -- before each tile.
   const uint16_t *kseq = a.keys + (size_t)a.seq * a.Lmax * kD;
   auto load_tile = [&](int kt, uint4 (&kr)[LPT]) {
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int key = kt + (NT / 16) * i + (tid >> 4);
-      kr[i] = key < kend ? load_nt16(kseq + (size_t)key * kD + (tid & 15) * 8)
-                         : make_uint4(0, 0, 0, 0);
+      const int key = min(kt + (NT / 16) * i + (tid >> 4), kend - 1);
+      kr[i] = load_nt16(kseq + (size_t)key * kD + (tid & 15) * 8);
     }
   };
   const f32x16 zero = {};
   uint4 kr[LPT];
-  if (k0 < kend) load_tile(k0, kr);
+  const int ntile = kend > k0 ? (kend - k0 + KT - 1) / KT : 0;
+  // tiles [0, nfull) lie below every query's position: no mask
+  const int nfull = kfull > k0 ? min(ntile, (kfull - k0) / KT) : 0;
+  if (ntile > 0) load_tile(k0, kr);
   int buf = 0;
-  for (int kt = k0; kt < kend; kt += KT, buf ^= 1) {
+  auto run_tile = [&](int it, auto full_tag) {
+    const int kt = k0 + it * KT;
     char *lt = (char *)ktile[buf];
 #pragma unroll
     for (int i = 0; i < LPT; ++i)
       *(uint4 *)(lt + ((NT / 16) * i + (tid >> 4)) * kPfRowLds + (tid & 15) * 16) = kr[i];
     __syncthreads();
-    if (kt + KT < kend) load_tile(kt + KT, kr);  // in flight during the MFMAs
+    load_tile(k0 + min(it + 1, ntile - 1) * KT, kr);  // in flight during the MFMAs
     // software pipeline over the tile's 32-key column blocks: the MFMA chain
     // of block c+1 is issued before the epilogue of block c, so the vector
     // ALU work overlaps the matrix core.  Tiles below every query's position
     // (FULL) take a straight-line body with unmasked stores.
-    auto tile_body = [&](auto full_tag) {
+    {
       constexpr bool FULL = decltype(full_tag)::value;
       auto chain = [&](int cb, f32x16 (&acc)[RT]) {
         const char *kr0 = lt + (cb * 32 + l32) * kPfRowLds + g * 16;
-        {
-          const uint4 bv = *(const uint4 *)kr0;
+        // the block's eight B fragments are read before its MFMAs issue
+        uint4 bvs[8];
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32(qa[rt][0], as_bf16x8(bv), zero);
-        }
+        for (int s = 0; s < 8; ++s) bvs[s] = *(const uint4 *)(kr0 + s * 32);
 #pragma unroll
-        for (int s = 1; s < 8; ++s) {
-          const uint4 bv = *(const uint4 *)(kr0 + s * 32);
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32(qa[rt][0], as_bf16x8(bvs[0]), zero);
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32(qa[rt][s], as_bf16x8(bv), acc[rt]);
-        }
+        for (int s = 1; s < 8; ++s)
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) acc[rt] = mfma32(qa[rt][s], as_bf16x8(bvs[s]), acc[rt]);
       };
       auto epilogue = [&](int cb, const f32x16 (&acc)[RT]) {
         const int kb = kt + cb * 32;  // this lane's key is kb + l32
@@ -186,12 +194,15 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a) {
         }
       }
       if ((KT / 32) & 1) epilogue(KT / 32 - 1, acc0); else epilogue(KT / 32 - 1, acc1);
-    };
-    if (kt + KT <= kfull)  // uniform
-      tile_body(std::true_type{});
-    else
-      tile_body(std::false_type{});
-  }
+    }
+    buf ^= 1;
+  };
+  // The first full tile is peeled: the loop is then entered, like its back
+  // edge, with one tile's loads and then its 16 score stores in flight, so
+  // the wait at its top is for the loads alone.
+  if (nfull > 0) run_tile(0, std::true_type{});
+  for (int it = 1; it < nfull; ++it) run_tile(it, std::true_type{});
+  for (int it = nfull; it < ntile; ++it) run_tile(it, std::false_type{});
   // columns of this split past every query of the workgroup
   for (int qi = 0; qi < QWG; ++qi) {
     const int t = qt0 + qi;

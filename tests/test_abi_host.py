@@ -85,6 +85,12 @@ def test_validation_before_any_hip_call(lib):
     assert lib.misa_pool(None, 64, F, None) == ERR_NULL
     assert lib.misa_pool(ctypes.byref(batch(seq_lens=0)), 64, F, None) == ERR_NULL
     assert lib.misa_pool(ctypes.byref(b), 64, None, None) == ERR_NULL
+    assert lib.misa_pool_append(ctypes.byref(b), 64, None, 1, F, None) == ERR_NULL
+    assert lib.misa_pool_append(ctypes.byref(b), 64, F, 1, None, None) == ERR_NULL
+    assert lib.misa_pool_append(ctypes.byref(b), 64, F, -1, F, None) == ERR_SHAPE
+    assert lib.misa_pool_append(ctypes.byref(b), 0, F, 1, F, None) == ERR_SHAPE
+    assert lib.misa_pool_append(ctypes.byref(b), 64, F, 4097, F, None) == ERR_SHAPE
+    assert lib.misa_pool_append(ctypes.byref(batch(d=64)), 64, F, 1, F, None) == ERR_UNSUPPORTED
     assert lib.misa_route(ctypes.byref(batch(q=0)), F, 64, 8, 0, F, None, F, big, None) == ERR_NULL
     assert lib.misa_route(ctypes.byref(b), None, 64, 8, 0, F, None, F, big, None) == ERR_NULL
     assert lib.misa_score_topk(ctypes.byref(b), None, 0, 8, None, None, F, big, None) == ERR_NULL

@@ -223,6 +223,64 @@ def test_score_topk(S, Lmax, T, H, seed, k):
     assert np.array_equal(np.sort(di, 1), np.sort(np_(dref), 1))
 
 
+# ------------------------------------------------------- pooled-cache append
+@pytest.mark.parametrize("B", [1, 16, 64, 128])
+def test_pool_append_matches_fresh_pool(B):
+    """After keys are appended, misa_pool_append rewrites only the blocks
+    that hold them; the cache then equals a fresh misa_pool bit for bit and
+    the oracle's pooling to fp32 accuracy, and blocks past the new lengths
+    are left untouched."""
+    abi = _abi()
+    S, Lmax = 3, 1000
+    case = synth.random_case(S, Lmax, 2, 8, seed=B)
+    old = np.array([100, 383, 700], np.int32)
+    new = old + np.array([1, 50, 129], np.int32)
+    case["seq_lens"] = old.copy()
+    b = upload(case)
+    pooled = abi.pool(b, B)
+    sentinel = 12345.0
+    M = (Lmax + B - 1) // B
+    nb_new = (new + B - 1) // B
+    for s_ in range(S):  # blocks past the new length must not be written
+        pooled[s_, nb_new[s_]:] = sentinel
+    b.seq_lens.copy_(torch.from_numpy(new))
+    abi.pool_append(b, B, torch.from_numpy(old).cuda(), int((new - old).max()), pooled)
+    fresh = abi.pool(b, B)
+    got, ref = np_(pooled), np_(fresh)
+    for s_ in range(S):
+        n = nb_new[s_]
+        assert np.array_equal(got[s_, :n], ref[s_, :n])
+        assert np.all(got[s_, n:] == sentinel)
+    case["seq_lens"] = new
+    opool = orc.pool(orc.Batch.from_case(case), B)
+    for s_ in range(S):
+        n = nb_new[s_]
+        assert np.allclose(got[s_, :n], opool[s_, :n], rtol=1e-5, atol=1e-6)
+
+
+def test_pool_append_streaming_decode():
+    """One key per step for 300 steps (the decode loop the append serves):
+    the cache stays equal to a fresh pool, and so does the router."""
+    abi = _abi()
+    S, Lmax, B, H = 2, 700, 16, 16
+    case = synth.random_case(S, Lmax, S, H, seed=7, q_seq=np.arange(S, dtype=np.int32),
+                             q_pos=np.full(S, 399, np.int32))
+    lens = np.array([100, 250], np.int32)
+    case["seq_lens"] = lens.copy()
+    b = upload(case)
+    pooled = abi.pool(b, B)
+    for _ in range(300):
+        old = torch.from_numpy(lens.copy()).cuda()
+        lens = lens + 1
+        b.seq_lens.copy_(torch.from_numpy(lens))
+        abi.pool_append(b, B, old, 1, pooled)
+    fresh = abi.pool(b, B)
+    assert np.array_equal(np_(pooled), np_(fresh))
+    h1 = np_(abi.route(b, pooled, B, 4, 0))
+    h2 = np_(abi.route(b, fresh, B, 4, 0))
+    assert np.array_equal(h1, h2)
+
+
 # --------------------------------------------------------------------- router
 @pytest.mark.parametrize("S,Lmax,T,H,seed", CASES)
 @pytest.mark.parametrize("B", [1, 16, 64, 128])
