@@ -349,6 +349,29 @@ def test_route_prefill_tiles(Lmax, T, H, B, positions, mode):
                     "router heads differ at margin %g" % parity.head_margin(og[t], h)
 
 
+# ------------------------------------------------------- selection fidelity
+def test_fidelity_sweep_matches_oracle_selections():
+    """The GPU sweep's recall / IoU against the dense set equal the same
+    metrics taken on the oracle's selections, and the invariants hold:
+    MISA with h = H and MISA-dagger with k' >= L reproduce DSA exactly."""
+    from long_context_sparse_05_amd import fidelity
+    S, L, H, k = 4, 3000, 16, 100
+    case = synth.decode_case(S, L, H, seed=5, n_needles=8)
+    rows = fidelity.sweep(case, k, hs=[1, 4, H], kps=[400, L], Bs=[16, 64])
+    ob = orc.Batch.from_case(case)
+    dense, _ = orc.dsa(ob, k)
+    for r in rows:
+        if r["method"] == "MISA":
+            sel = orc.misa(ob, r["B"], r["h"], k)["idx"]
+        else:
+            sel = orc.misa_dagger(ob, r["B"], r["h"], r["kp"], k)["idx"]
+        orr, ori = fidelity.set_metrics(sel, dense)
+        # a near-tie at the k-th boundary may swap one token of a row
+        assert abs(r["recall"] - orr) <= 1.5 / k and abs(r["iou"] - ori) <= 3.0 / k, (r, orr, ori)
+        if r["h"] == H or r["kp"] >= L:
+            assert r["recall"] == 1.0 and r["iou"] == 1.0, r
+
+
 # --------------------------------------------------------------------- rerank
 @pytest.mark.parametrize("S,Lmax,T,H,seed", CASES[:4])
 def test_rerank(S, Lmax, T, H, seed):
