@@ -19,7 +19,9 @@
  *   [MISA-AB]  The MISA abstract, printed on the thelatestinai page titled
  *              "HISA: Efficient Hierarchical Indexing for Fine-Grained
  *              Sparse Attention" (first paragraph).
- *   [HISA-AB]  "HISA" abstract on the Lattice page for arXiv 2603.28458.
+ *   [HISA-AB]  "HISA" abstract on the Lattice page for arXiv 2603.28458, and
+ *              the aiqbench page "HISA: Efficient Hierarchical Indexing for
+ *              Fine-Grained Sparse Attention" (v4 abstract).
  *
  * Readings taken where the pages are silent (each is repeated at its use):
  *   R1  the prefix of a query at position p is tokens 0..p (inclusive);
@@ -29,6 +31,7 @@
  *   R5  router affinity = ReLU(q_j . Kbar_b), aggregated by a sum over the
  *       query's blocks and multiplied by w_j (mode 0) or |w_j| (mode 1);
  *   R6  ties: larger value first, then the lower index; -0.0 equals +0.0.
+ *   H1-H4  the hierarchical indexer's readings, at orc_hisa.
  * The pages do not fix the functional forms R3 and R5: these readings are
  * this implementation's, and the tests pin the code to them (closed forms,
  * brute force, invariants, a hand-worked example), not to the pages.
@@ -425,5 +428,118 @@ int orc_misa_dagger(const uint16_t *keys, const uint16_t *q, const float *w,
   if (rc == ORC_OK)
     rc = orc_rerank(keys, q, w, q_seq, q_pos, S, Lmax, d, T, H, cc, kc, k, idx, val);
   if (!cand) free(cc);
+  return rc;
+}
+
+/*
+ * orc_hisa: the hierarchical block-to-token indexer ([HISA-AB]: a
+ * block-level coarse filter scores pooled block representations to discard
+ * irrelevant regions, then a token-level refinement applies the original
+ * indexer only within the retained candidate blocks; the token-level top-k
+ * pattern is kept).  Readings, the pages giving no formula:
+ *   H1  a block's representation is the mean of its keys (R4's blocks, as
+ *       MISA's router pools them); the query's own last block is the mean
+ *       over its prefix tokens;
+ *   H2  a block's score is the indexer's score form on that mean:
+ *       s_b = sum_{j in heads} w_j * max(0, q_j . Kbar_b), j ascending;
+ *   H3  the m blocks with the largest s_b are kept (R6 ties: lower block id);
+ *       m is a parameter, the pages giving no number;
+ *   H4  every prefix token of the kept blocks is scored with the same heads
+ *       (R3) and the top-k by R6 is the output, padded with -1.
+ * heads == NULL: all H heads (HISA).  heads [T][h]: those heads in both
+ * stages (the routed heads of MISA, for MISA composed with HISA).
+ *   idx [T][k]; val [T][k], blocks [T][m] (-1 padded) and
+ *   bscore [T][ceil(Lmax/B)] (-inf past the query's blocks) may be NULL.
+ */
+int orc_hisa(const uint16_t *keys, const uint16_t *q, const float *w,
+             const int32_t *q_seq, const int32_t *q_pos, int S, int Lmax, int d,
+             int T, int H, int B, int m, const int32_t *heads, int h, int k,
+             int32_t *idx, double *val, int32_t *blocks, double *bscore) {
+  if (!keys || !q || !w || !q_seq || !q_pos || !idx) return ORC_EINVAL;
+  if (S < 1 || Lmax < 1 || d < 1 || T < 0 || H < 1 || B < 1 || m < 1 || k < 1)
+    return ORC_EINVAL;
+  if (heads && (h < 1 || h > H)) return ORC_EINVAL;
+  const int nh = heads ? h : H;
+  const int Mmax = (Lmax + B - 1) / B;
+  for (int t = 0; t < T; ++t) {
+    if (q_seq[t] < 0 || q_seq[t] >= S || q_pos[t] < 0 || q_pos[t] >= Lmax) return ORC_EINVAL;
+    for (int r = 0; heads && r < h; ++r)
+      if (heads[(size_t)t * h + r] < 0 || heads[(size_t)t * h + r] >= H) return ORC_EINVAL;
+  }
+  int rc = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int t = 0; t < T; ++t) {
+    const int n = q_pos[t] + 1;
+    const int M = (n + B - 1) / B;
+    const uint16_t *ks = keys + (size_t)q_seq[t] * Lmax * d;
+    int32_t *hs = (int32_t *)malloc(sizeof(int32_t) * (size_t)nh);
+    double *kbar = (double *)malloc(sizeof(double) * (size_t)M * d);
+    double *s = (double *)malloc(sizeof(double) * (size_t)M);
+    int32_t *kept = (int32_t *)malloc(sizeof(int32_t) * (size_t)m);
+    orc_item *it = (orc_item *)malloc(sizeof(orc_item) * ((size_t)m * B + 1));
+    if (!hs || !kbar || !s || !kept || !it) {
+#pragma omp atomic write
+      rc = ORC_ENOMEM;
+      free(hs); free(kbar); free(s); free(kept); free(it);
+      continue;
+    }
+    for (int r = 0; r < nh; ++r) hs[r] = heads ? heads[(size_t)t * h + r] : r;
+    qsort(hs, (size_t)nh, sizeof(int32_t), orc_cmp_int);
+    /* H1: block means; the last block holds the prefix tokens in it */
+    for (int b = 0; b < M; ++b) {
+      int lo = b * B, hi = lo + B < n ? lo + B : n;
+      for (int c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int i = lo; i < hi; ++i) acc += orc_bf16(ks[(size_t)i * d + c]);
+        kbar[(size_t)b * d + c] = acc / (double)(hi - lo);
+      }
+    }
+    /* H2: block scores */
+    for (int b = 0; b < M; ++b) {
+      double sb = 0.0;
+      for (int r = 0; r < nh; ++r) {
+        const int j = hs[r];
+        const uint16_t *qj = q + ((size_t)t * H + j) * d;
+        double x = 0.0;
+        for (int c = 0; c < d; ++c) x += orc_bf16(qj[c]) * kbar[(size_t)b * d + c];
+        sb += (double)w[(size_t)t * H + j] * (x > 0.0 ? x : 0.0);
+      }
+      s[b] = sb;
+    }
+    if (bscore)
+      for (int b = 0; b < Mmax; ++b) bscore[(size_t)t * Mmax + b] = b < M ? s[b] : -INFINITY;
+    /* H3: the m best blocks */
+    if (orc_topk(s, M, m, kept, NULL) != ORC_OK) {
+#pragma omp atomic write
+      rc = ORC_ENOMEM;
+    } else {
+      if (blocks) memcpy(blocks + (size_t)t * m, kept, sizeof(int32_t) * (size_t)m);
+      /* H4: the indexer over the kept blocks' prefix tokens */
+      int nv = 0;
+      for (int r = 0; r < m; ++r) {
+        const int b = kept[r];
+        if (b < 0) continue;
+        const int lo = b * B, hi = lo + B < n ? lo + B : n;
+        for (int i = lo; i < hi; ++i) {
+          const uint16_t *kv = ks + (size_t)i * d;
+          double si = 0.0;
+          for (int rr = 0; rr < nh; ++rr) {
+            const int j = hs[rr];
+            double x = orc_dot_bf16(q + ((size_t)t * H + j) * d, kv, d);
+            si += (double)w[(size_t)t * H + j] * (x > 0.0 ? x : 0.0);
+          }
+          it[nv].v = si;
+          it[nv].i = i;
+          ++nv;
+        }
+      }
+      qsort(it, (size_t)nv, sizeof(orc_item), orc_cmp);
+      for (int r = 0; r < k; ++r) {
+        idx[(size_t)t * k + r] = r < nv ? (int32_t)it[r].i : -1;
+        if (val) val[(size_t)t * k + r] = r < nv ? it[r].v : -INFINITY;
+      }
+    }
+    free(hs); free(kbar); free(s); free(kept); free(it);
+  }
   return rc;
 }

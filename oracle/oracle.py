@@ -186,6 +186,24 @@ def rerank(b: Batch, cand, k):
     return idx, val
 
 
+def hisa(b: Batch, B, m, k, heads=None):
+    """The hierarchical block-to-token indexer (orc_hisa): all heads, or the
+    given heads [T][h] in both stages.  Returns dict(idx, val, blocks, bscore)."""
+    Mmax = (b.Lmax + B - 1) // B
+    idx = np.empty((b.T, k), np.int32)
+    val = np.empty((b.T, k), np.float64)
+    blocks = np.empty((b.T, m), np.int32)
+    bscore = np.empty((b.T, Mmax), np.float64)
+    if heads is None:
+        ph, h = None, 0
+    else:
+        heads, ph = _c(heads, np.int32)
+        h = heads.shape[1]
+    _check(lib().orc_hisa(*b.head(), B, m, ph, h, k, idx.ctypes.data_as(_P), val.ctypes.data_as(_P),
+                          blocks.ctypes.data_as(_P), bscore.ctypes.data_as(_P)), "hisa")
+    return dict(idx=idx, val=val, blocks=blocks, bscore=bscore)
+
+
 def misa_dagger(b: Batch, B, h, kc, k, mode=0):
     heads = np.empty((b.T, h), np.int32)
     cand = np.empty((b.T, kc), np.int32)

@@ -328,3 +328,95 @@ def test_needles_are_selected():
     norms = np.linalg.norm(kf, axis=1)
     needles = np.argsort(-norms)[:16]
     assert np.isin(needles, idx[b.T - 1]).mean() > 0.5
+
+
+# ------------------------------------------------- hierarchical indexer (HISA)
+def test_hisa_hand_worked_example():
+    g = json.load(open(GOLDEN))
+    e0, e1 = g["queries"]
+    b = _one_seq_batch(g["keys"], [e0["q"], e1["q"]], [e0["w"], e1["w"]], [e0["p"], e1["p"]])
+    B = g["B"]
+    r = orc.hisa(b, B, 1, 3)
+    np.testing.assert_array_equal(r["bscore"][0, :3], e0["hisa_block_scores"])
+    np.testing.assert_array_equal(r["bscore"][1, :3], e1["hisa_block_scores"])
+    assert list(r["blocks"][0]) == e0["hisa_m1_blocks"] and list(r["blocks"][1]) == e1["hisa_m1_blocks"]
+    assert list(r["idx"][0]) == e0["hisa_m1_top3"]
+    assert list(orc.hisa(b, B, 1, 2)["idx"][1]) == e1["hisa_m1_top2"]
+    r2 = orc.hisa(b, B, 2, 3)
+    assert list(r2["blocks"][0]) == e0["hisa_m2_blocks"] and list(r2["blocks"][1]) == e1["hisa_m2_blocks"]
+    assert list(r2["idx"][0]) == e0["hisa_m2_top3"]
+    assert list(orc.hisa(b, B, 2, 2)["idx"][1]) == e1["hisa_m2_top2"]
+    # routed heads in both stages
+    rh = orc.hisa(b, B, 1, 2, heads=np.array([[0], [1]], np.int32))
+    assert list(rh["idx"][0][:1]) == e0["misa_hisa_head0_m1_top1"]
+    assert list(rh["idx"][1]) == e1["misa_hisa_head1_m1_top2"]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_hisa_keeping_every_block_is_dsa(seed):
+    """m >= the query's block count: the refinement sees the whole prefix, so
+    HISA is the dense indexer, bit for bit."""
+    b, _ = _rand(seed)
+    for B in (1, 7, 64):
+        M = (b.Lmax + B - 1) // B
+        r = orc.hisa(b, B, M, 50)
+        idx, val = orc.dsa(b, 50)
+        assert np.array_equal(r["idx"], idx) and np.array_equal(r["val"], val)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_hisa_unit_blocks_is_dsa(seed):
+    """B = 1: a block's mean is its one key, so block scores are token scores
+    and the m >= k best blocks contain the dense top-k."""
+    b, _ = _rand(seed)
+    for k, m in ((10, 10), (20, 37)):
+        r = orc.hisa(b, 1, m, k)
+        idx, val = orc.dsa(b, k)
+        assert np.array_equal(r["idx"], idx) and np.array_equal(r["val"], val)
+        sc = orc.scores(b)
+        for t in range(b.T):
+            n = b.q_pos[t] + 1
+            np.testing.assert_array_equal(r["bscore"][t, :n], sc[t, :n])
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_hisa_with_every_head_routed_is_hisa(seed):
+    """Routing every head (in any order) changes nothing."""
+    b, _ = _rand(seed)
+    rng = np.random.default_rng(seed)
+    heads = np.stack([rng.permutation(b.H) for _ in range(b.T)]).astype(np.int32)
+    for B, m in ((8, 3), (32, 2)):
+        a = orc.hisa(b, B, m, 40)
+        c = orc.hisa(b, B, m, 40, heads=heads)
+        for key in ("idx", "val", "blocks", "bscore"):
+            assert np.array_equal(a[key], c[key]), key
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_hisa_single_head_block_scores_sum_to_router_importance(seed):
+    """With one head j in both stages and w_j > 0, the block scores are
+    w_j * ReLU(q_j . Kbar_b); their sum over the query's blocks is the
+    router's importance g_j (mode 0), computed by the router's own code."""
+    b, _ = _rand(seed)
+    B = 16
+    _, g = orc.route(b, B, 1, 0)
+    for j in range(b.H):
+        heads = np.full((b.T, 1), j, np.int32)
+        r = orc.hisa(b, B, 1, 5, heads=heads)
+        for t in range(b.T):
+            M = (b.q_pos[t] + 1 + B - 1) // B
+            assert np.isclose(r["bscore"][t, :M].sum(), g[t, j], rtol=1e-12, atol=1e-12)
+            assert np.all(np.isneginf(r["bscore"][t, M:]))
+
+
+def test_hisa_constant_keys_closed_form():
+    """All keys equal: every block and every token score is the same, so the
+    first m blocks are kept and the top-k is the first k tokens."""
+    L, d, B, m, k = 200, 4, 16, 3, 20
+    keys = np.tile(np.array([1.0, -0.5, 0.25, 2.0], np.float32), (L, 1))
+    b = _one_seq_batch(keys, [[[0.5, 1.0, -1.0, 0.25], [1.0, 0.0, 0.0, 0.0]]], [[0.7, -0.2]], [150])
+    r = orc.hisa(b, B, m, k)
+    assert list(r["blocks"][0]) == [0, 1, 2]
+    assert list(r["idx"][0]) == list(range(k))
+    x0, x1 = 0.5 - 0.5 - 0.25 + 0.5, 1.0
+    assert np.allclose(r["val"][0], 0.7 * max(x0, 0) - 0.2 * max(x1, 0))
