@@ -159,6 +159,12 @@ def cpu_baseline_rows(case, cfg, rows, reps=3):
         t0 = time.perf_counter()
         if kind == "dagger":
             out = orc.misa_dagger(b, cfg["B"], cfg["h"], cfg["kc"], cfg["k"])
+        elif kind == "hisa":
+            out = orc.hisa(b, cfg["B"], cfg["m"], cfg["k"])
+        elif kind == "misa_hisa":
+            heads, _ = orc.route(b, cfg["B"], cfg["h"])
+            out = orc.hisa(b, cfg["B"], cfg["m"], cfg["k"], heads=heads)
+            out["heads"] = heads
         elif "h" in cfg:
             out = orc.misa(b, cfg["B"], cfg["h"], cfg["k"])
         else:
@@ -201,8 +207,10 @@ def main(argv=None):
     case, cfg = synth.make_workload(args.workload, seed=0)
     kind = cfg["kind"]
     routed = "h" in cfg
+    hier = kind in ("hisa", "misa_hisa")  # the hierarchical indexer's step
     B, h, k = cfg.get("B"), cfg.get("h"), cfg["k"]
     kc = cfg.get("kc", k)
+    m = cfg.get("m")
     b = abi.Batch.from_numpy(case)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
@@ -212,7 +220,7 @@ def main(argv=None):
 
     pool_us = None
     pooled = None
-    if routed:  # once per key cache: block pooling
+    if B is not None:  # once per key cache: block pooling
         pooled = abi.pool(b, B)
         e0, e1 = ev.create(), ev.create()
         ev.record(e0, sp)
@@ -227,7 +235,10 @@ def main(argv=None):
     val = torch.empty((b.T, k1), dtype=torch.float32, device=dev)
     fin = torch.empty((b.T, k), dtype=torch.int32, device=dev)
     fin_val = torch.empty((b.T, k), dtype=torch.float32, device=dev)
-    if routed:
+    if hier:
+        ws_h = b.workspace(abi.MISA_OP_HISA, B=B, h=h or 1, k=k, kc=m)
+        ws_r = b.workspace(abi.MISA_OP_ROUTE, B=B, h=h) if routed else None
+    elif routed:
         ws_i = b.workspace(abi.MISA_OP_INDEXER, B=B, h=h, k=k1)
         ws_r = b.workspace(abi.MISA_OP_ROUTE, B=B, h=h)
         ws_s = b.workspace(abi.MISA_OP_SCORE_TOPK, h=h, k=k1)
@@ -236,7 +247,12 @@ def main(argv=None):
     ws_rr = b.workspace(abi.MISA_OP_RERANK, k=k, kc=kc) if kind == "dagger" else None
 
     def step(events=None):
-        if routed:  # the fused call: router, routed scoring, top-k (k' for MISA-dagger)
+        if hier:  # (router, then) block scores, kept blocks, refinement, top-k
+            if routed:
+                abi.route(b, pooled, B, h, 0, heads=heads, ws=ws_r)
+            abi.hisa_indexer(b, pooled, B, m, k, heads=heads, idx=idx, val=val, ws=ws_h,
+                             events=events)
+        elif routed:  # the fused call: router, routed scoring, top-k (k' for MISA-dagger)
             abi.indexer(b, pooled, B, h, k1, heads=heads, idx=idx, val=val, ws=ws_i, events=events)
             if kind == "dagger":  # fine stage: all-head rescoring of the k' candidates
                 abi.rerank(b, idx, k, idx=fin, val=fin_val, ws=ws_rr)
@@ -272,7 +288,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     score_ms = float(np.mean([ev.ms(a, c) for a, c in sev]))
     ms_sep = None
-    if routed:
+    if routed and not hier:
         for _ in range(args.warmup):
             step_separate()
         ev.record(t_start, sp)
@@ -308,6 +324,16 @@ def main(argv=None):
                 "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
                 "kernel": "score_prefill_kernel (32x32x16 bf16 MFMA, %d routed heads)" % nh,
                 "alg_flops_per_launch": flops}
+    elif hier:
+        # the refinement kernel gathers the candidate keys of the kept blocks
+        qp = case["q_pos"].astype(np.int64)
+        n_cand = int(np.minimum(m * B, qp + 1).sum())
+        alg_bytes = n_cand * KEY_BYTES + b.T * nh * KEY_BYTES
+        achieved = alg_bytes / (score_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "kernel": "score_rows_kernel (gathered candidate rows, %d heads)" % nh,
+                "alg_bytes_per_launch": alg_bytes}
     else:
         alg_bytes = n_keys * KEY_BYTES + b.T * nh * KEY_BYTES  # keys streamed + query rows
         achieved = alg_bytes / (score_ms * 1e-3) / 1e9
@@ -339,11 +365,13 @@ def main(argv=None):
     }
     if kind == "dagger":
         res["config"]["k_prime"] = kc
+    if hier:
+        res["config"]["kept_blocks"] = m
     if ms_sep is not None:
         res["us_per_batch_separate_calls"] = ms_sep * 1e3
     if pool_us is not None:
         res["pool_us_once_per_cache"] = pool_us
-    if kind != "prefill":
+    if kind != "prefill" and not hier:
         # whole step: keys, complete pooled blocks and all head queries read;
         # selected ids and scores written
         n_blocks = int((case["q_pos"].astype(np.int64) // B).sum()) if routed else 0

@@ -97,6 +97,7 @@ typedef struct misa_batch {
 #define MISA_OP_RERANK 3      /* misa_rerank                          */
 #define MISA_OP_TOPK 4        /* misa_topk (b->T rows of b->Lmax)     */
 #define MISA_OP_INDEXER 5     /* misa_indexer                         */
+#define MISA_OP_HISA 6        /* hisa_indexer, hisa_blocks (kc = m)   */
 
 /*
  * misa_workspace_bytes: device workspace needed by operation `op` for this
@@ -252,6 +253,47 @@ int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B,
                     float *head_score, int32_t *idx, float *val, void *ws,
                     size_t ws_bytes, void *stream, void *ev_start,
                     void *ev_stop);
+
+/*
+ * hisa_indexer -- the hierarchical block-to-token indexer ("HISA: Efficient
+ * Hierarchical Indexing for Fine-Grained Sparse Attention", abstract: a
+ * block-level coarse filter scores pooled block representations and
+ * discards irrelevant regions, then the original indexer runs only within
+ * the retained candidate blocks; the token-level top-k output is kept).
+ * Readings, the pages giving no formula: a block's representation is its
+ * mean key (misa_pool's cache; the query's own last block is the mean over
+ * [floor(p/B)*B, p]); its score is the indexer's form on that mean,
+ *   s_b = sum_{j in heads} w_j * max(0, q_j . Kbar_b);
+ * the m blocks with the largest s_b are kept (ties: lower block id); every
+ * prefix token of the kept blocks is scored with the same heads and the
+ * top-k by (score desc, token id asc) is written, padded with -1 / -inf.
+ *   pooled  misa_pool's output for the same keys and B.
+ *   m       kept blocks, 1 <= m <= ceil(Lmax/B) (not on the pages).
+ *   heads   NULL: all H heads (HISA; h must be 0).  int32 [T][h] (device):
+ *           these heads in both stages -- the routed heads of misa_route,
+ *           giving MISA composed with HISA (head axis, then token axis).
+ *   idx/val [T][k] (val may be NULL).  Workspace: misa_workspace_bytes with
+ *           MISA_OP_HISA, kc = m.  1 <= k <= Lmax.
+ */
+int hisa_indexer(const misa_batch *b, const float *pooled, int32_t B, int32_t m,
+                 const int32_t *heads, int32_t h, int32_t k, int32_t *idx, float *val, void *ws,
+                 size_t ws_bytes, void *stream);
+
+/* hisa_indexer with hipEvent_t handles recorded around the token-level
+ * scoring kernel (measurement hook; either may be NULL). */
+int hisa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t m,
+                    const int32_t *heads, int32_t h, int32_t k, int32_t *idx, float *val, void *ws,
+                    size_t ws_bytes, void *stream, void *ev_start, void *ev_stop);
+
+/*
+ * hisa_blocks -- hisa_indexer's coarse stage alone: block scores
+ * fp32 [T][ceil(Lmax/B)] (-inf past the query's floor(p/B)+1 blocks; may be
+ * NULL) and the m kept block ids int32 [T][m] (a set, -1 padded; may be
+ * NULL).  Same arguments and workspace as hisa_indexer (k unused).
+ */
+int hisa_blocks(const misa_batch *b, const float *pooled, int32_t B, int32_t m,
+                const int32_t *heads, int32_t h, float *block_scores, int32_t *blocks, void *ws,
+                size_t ws_bytes, void *stream);
 
 /* misa_status_str -- a static English description of a status code. */
 const char *misa_status_str(int status);

@@ -17,12 +17,14 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmisa_indexer.so")
 
-MISA_OP_DENSE, MISA_OP_ROUTE, MISA_OP_SCORE_TOPK, MISA_OP_RERANK, MISA_OP_TOPK, MISA_OP_INDEXER = range(6)
+(MISA_OP_DENSE, MISA_OP_ROUTE, MISA_OP_SCORE_TOPK, MISA_OP_RERANK, MISA_OP_TOPK, MISA_OP_INDEXER,
+ MISA_OP_HISA) = range(7)
 
 # Every entry point include/misa_indexer.h declares.
 EXPORTS = ("misa_workspace_bytes", "misa_pool", "misa_pool_append", "misa_route", "misa_score", "misa_topk",
            "misa_score_topk", "misa_score_topk_ev", "indexer_dense", "misa_rerank",
-           "misa_indexer", "misa_indexer_ev", "misa_status_str")
+           "misa_indexer", "misa_indexer_ev", "hisa_indexer", "hisa_indexer_ev", "hisa_blocks",
+           "misa_status_str")
 
 
 class MisaBatch(ctypes.Structure):
@@ -264,6 +266,42 @@ def indexer(batch: Batch, pooled, B: int, h: int, k: int, mode: int = 0, heads=N
                                       _ptr(ws), nws, _stream(stream), ctypes.c_void_p(events[0]),
                                       ctypes.c_void_p(events[1])), "misa_indexer_ev")
     return heads, idx, val
+
+
+def hisa_indexer(batch: Batch, pooled, B: int, m: int, k: int, heads=None, idx=None, val=None,
+                 want_val=True, ws=None, stream=None, events=None):
+    """hisa_indexer: block scores, the m best blocks, the indexer over their
+    tokens, top-k.  heads=None uses all heads; an int32 [T][h] tensor uses
+    those heads in both stages (MISA composed with HISA).  Returns (idx, val)."""
+    torch = _torch()
+    idx, val = _sel_out(batch.T, k, batch.keys.device, idx, val, want_val)
+    h = 0 if heads is None else heads.shape[1]
+    if heads is not None:
+        _need(heads, torch.int32, "heads", 2)
+    ws, nws = _ws(batch, ws, MISA_OP_HISA, B=B, h=max(h, 1), k=k, kc=m)
+    args = (ctypes.byref(batch.c), _ptr(pooled), B, m, _ptr(heads), h, k, _ptr(idx), _ptr(val),
+            _ptr(ws), nws, _stream(stream))
+    if events is None:
+        _check(load().hisa_indexer(*args), "hisa_indexer")
+    else:
+        _check(load().hisa_indexer_ev(*args, ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1])),
+               "hisa_indexer_ev")
+    return idx, val
+
+
+def hisa_blocks(batch: Batch, pooled, B: int, m: int, heads=None, ws=None, stream=None):
+    """hisa_indexer's coarse stage: (block_scores [T][ceil(Lmax/B)], kept
+    blocks [T][m], a set)."""
+    torch = _torch()
+    dev = batch.keys.device
+    M = (batch.Lmax + B - 1) // B
+    scores = torch.empty((batch.T, M), dtype=torch.float32, device=dev)
+    blocks = torch.empty((batch.T, m), dtype=torch.int32, device=dev)
+    h = 0 if heads is None else heads.shape[1]
+    ws, nws = _ws(batch, ws, MISA_OP_HISA, B=B, h=max(h, 1), k=1, kc=m)
+    _check(load().hisa_blocks(ctypes.byref(batch.c), _ptr(pooled), B, m, _ptr(heads), h, _ptr(scores),
+                              _ptr(blocks), _ptr(ws), nws, _stream(stream)), "hisa_blocks")
+    return scores, blocks
 
 
 def rerank(batch: Batch, cand, k: int, idx=None, val=None, want_val=True, ws=None, stream=None):

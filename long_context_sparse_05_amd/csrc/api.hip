@@ -83,6 +83,34 @@ size_t route_bytes(const misa_batch *b, int B) {
   return align_up((size_t)b->T * (nchunks + 1) * b->H * sizeof(float));
 }
 
+// The hierarchical indexer's workspace: block scores, block counts, kept
+// blocks, candidate tokens, then the block select and the token select.
+struct HisaLayout {
+  size_t bscore, mt, kept, cand, bsel, tsel, total;
+  SelectLayout LB, LT;
+};
+HisaLayout hisa_layout(const misa_batch *b, int B, int m, int k) {
+  HisaLayout H;
+  const size_t T = (size_t)b->T, Mmax = (size_t)(b->Lmax + B - 1) / B, kc = (size_t)m * B;
+  size_t off = 0;
+  H.bscore = off;
+  off = align_up(off + T * Mmax * sizeof(float));
+  H.mt = off;
+  off = align_up(off + T * sizeof(int32_t));
+  H.kept = off;
+  off = align_up(off + T * (size_t)m * sizeof(int32_t));
+  H.cand = off;
+  off = align_up(off + T * kc * sizeof(int32_t));
+  H.LB = select_layout(T, Mmax, m, false);
+  H.bsel = off;
+  off = align_up(off + H.LB.total);
+  H.LT = select_layout(T, kc, k, true);
+  H.tsel = off;
+  off = align_up(off + H.LT.total);
+  H.total = off;
+  return H;
+}
+
 int score_chunk(int rows, int ncols) {
   // about 512 workgroups over the whole launch (two per CU), 256..4096 columns each
   const size_t work = (size_t)rows * ncols;
@@ -123,16 +151,20 @@ PrefillArgs make_prefill_args(const misa_batch *b, const int32_t *heads, int h, 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MISA_OK : MISA_ERR_HIP; }
 
-// Selection over rows of ld columns.  Few rows: zero the histograms ->
+// Selection over rows of ld columns.  Few long rows: zero the histograms ->
 // [score rows + histogram | histogram] -> multi-workgroup filter -> finish.
-// Enough rows to fill the GPU: [score rows] -> one workgroup per row.
+// Enough rows to fill the GPU, or short rows: [score rows] -> one workgroup
+// per row.
 constexpr int kRowSelectMinRows = 256;
+// Rows this short are one workgroup's work whatever their number: a single
+// select kernel beats the fill + histogram + filter + finish chain.
+constexpr int kRowSelectMaxShortRow = 16384;
 
 int run_select(const ScoreArgs *score, const float *scores_in, int rows, int ld,
                const int32_t *row_len, int row_len_add, const int32_t *map, int k,
                int32_t *idx, float *val, void *ws, const SelectLayout &L, hipStream_t st,
                void *ev_start = nullptr, void *ev_stop = nullptr, bool zeroed = false) {
-  const bool row_mode = rows >= kRowSelectMinRows;
+  const bool row_mode = rows >= kRowSelectMinRows || ld <= kRowSelectMaxShortRow;
   uint32_t *hist = (uint32_t *)((char *)ws + L.hist);
   hipError_t e = hipSuccess;
   if (!zeroed && !row_mode) {  // the fused indexer call clears these in its router kernel
@@ -229,6 +261,12 @@ int misa_workspace_bytes(const misa_batch *b, int32_t op, int32_t B, int32_t h, 
       if (k < 1) return MISA_ERR_SHAPE;
       *bytes = select_layout(b->T, b->Lmax, k, false).total;
       return MISA_OK;
+    case MISA_OP_HISA: {  // kc carries m, the number of kept blocks
+      const int Mmax = B >= 1 ? (b->Lmax + B - 1) / B : 0;
+      if (B < 1 || B > b->Lmax || kc < 1 || kc > Mmax || k < 1 || k > b->Lmax) return MISA_ERR_SHAPE;
+      *bytes = hisa_layout(b, B, kc, k).total;
+      return MISA_OK;
+    }
     default:
       return MISA_ERR_SHAPE;
   }
@@ -438,6 +476,98 @@ int misa_rerank(const misa_batch *b, const int32_t *cand, int32_t kc, int32_t k,
   s.chunk = score_chunk(b->T, kc);
   return run_select(&s, nullptr, b->T, kc, nullptr, 0, cand, k, idx, val, ws, L,
                     (hipStream_t)stream);
+}
+
+static HisaArgs make_hisa_args(const misa_batch *b, const float *pooled, int B, const int32_t *heads,
+                               int h, void *ws, const HisaLayout &HL, float *bscore) {
+  HisaArgs a{};
+  a.keys = b->keys;
+  a.q = b->q;
+  a.w = b->w;
+  a.q_seq = b->q_seq;
+  a.q_pos = b->q_pos;
+  a.pooled = pooled;
+  a.heads = heads;
+  a.bscore = bscore ? bscore : (float *)((char *)ws + HL.bscore);
+  a.mt = (int32_t *)((char *)ws + HL.mt);
+  a.S = b->S;
+  a.Lmax = b->Lmax;
+  a.T = b->T;
+  a.H = b->H;
+  a.nh = heads ? h : b->H;
+  a.B = B;
+  a.Mmax = (b->Lmax + B - 1) / B;
+  a.nchunks = (a.Mmax + kRouteChunk - 1) / kRouteChunk;
+  return a;
+}
+
+static int hisa_check(const misa_batch *b, const float *pooled, int B, int m, const int32_t *heads,
+                      int h, int k) {
+  int rc = check_batch(b, true);
+  if (rc) return rc;
+  if (!pooled) return MISA_ERR_NULL;
+  if (B < 1 || B > b->Lmax) return MISA_ERR_SHAPE;
+  const int Mmax = (b->Lmax + B - 1) / B;
+  if (m < 1 || m > Mmax || k < 1 || k > b->Lmax) return MISA_ERR_SHAPE;
+  if (heads ? (h < 1 || h > b->H) : h != 0) return MISA_ERR_SHAPE;
+  return MISA_OK;
+}
+
+// block scores and the m kept blocks (the coarse stage alone)
+static int hisa_coarse(const misa_batch *b, const float *pooled, int B, int m, const int32_t *heads,
+                       int h, void *ws, const HisaLayout &HL, int32_t *kept, float *bscore,
+                       hipStream_t st) {
+  const HisaArgs a = make_hisa_args(b, pooled, B, heads, h, ws, HL, bscore);
+  if (launch_hisa_blocks(a, st) != hipSuccess) return MISA_ERR_HIP;
+  return run_select(nullptr, a.bscore, b->T, a.Mmax, a.mt, 0, nullptr, m, kept, nullptr,
+                    (char *)ws + HL.bsel, HL.LB, st);
+}
+
+int hisa_blocks(const misa_batch *b, const float *pooled, int32_t B, int32_t m,
+                const int32_t *heads, int32_t h, float *block_scores, int32_t *blocks, void *ws,
+                size_t ws_bytes, void *stream) {
+  int rc = hisa_check(b, pooled, B, m, heads, h, 1);
+  if (rc) return rc;
+  if (!ws) return MISA_ERR_NULL;
+  const HisaLayout HL = hisa_layout(b, B, m, 1);
+  if (ws_bytes < HL.total) return MISA_ERR_WORKSPACE;
+  const hipStream_t st = (hipStream_t)stream;
+  int32_t *kept = blocks ? blocks : (int32_t *)((char *)ws + HL.kept);
+  return hisa_coarse(b, pooled, B, m, heads, h, ws, HL, kept, block_scores, st);
+}
+
+int hisa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t m,
+                    const int32_t *heads, int32_t h, int32_t k, int32_t *idx, float *val, void *ws,
+                    size_t ws_bytes, void *stream, void *ev_start, void *ev_stop) {
+  int rc = hisa_check(b, pooled, B, m, heads, h, k);
+  if (rc) return rc;
+  if (!idx || !ws) return MISA_ERR_NULL;
+  const HisaLayout HL = hisa_layout(b, B, m, k);
+  if (ws_bytes < HL.total) return MISA_ERR_WORKSPACE;
+  const hipStream_t st = (hipStream_t)stream;
+  int32_t *kept = (int32_t *)((char *)ws + HL.kept);
+  int32_t *cand = (int32_t *)((char *)ws + HL.cand);
+  rc = hisa_coarse(b, pooled, B, m, heads, h, ws, HL, kept, nullptr, st);
+  if (rc) return rc;
+  if (launch_hisa_expand(kept, b->q_pos, b->T, m, B, cand, st) != hipSuccess) return MISA_ERR_HIP;
+  // token-level refinement: the indexer over the kept blocks' tokens
+  const int kc = m * B;
+  void *tws = (char *)ws + HL.tsel;
+  ScoreArgs s = make_score_args(b, heads, heads ? h : b->H);
+  s.scores = (float *)((char *)tws + HL.LT.scores);
+  s.cand = cand;
+  s.ncols = kc;
+  s.ld = kc;
+  s.chunk = score_chunk(b->T, kc);
+  return run_select(&s, nullptr, b->T, kc, nullptr, 0, cand, k, idx, val, tws, HL.LT, st, ev_start,
+                    ev_stop);
+}
+
+int hisa_indexer(const misa_batch *b, const float *pooled, int32_t B, int32_t m,
+                 const int32_t *heads, int32_t h, int32_t k, int32_t *idx, float *val, void *ws,
+                 size_t ws_bytes, void *stream) {
+  return hisa_indexer_ev(b, pooled, B, m, heads, h, k, idx, val, ws, ws_bytes, stream, nullptr,
+                         nullptr);
 }
 
 }  // extern "C"

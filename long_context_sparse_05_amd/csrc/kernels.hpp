@@ -84,6 +84,23 @@ struct RouteArgs {
   int S, Lmax, T, H, B, h, mode, Mmax, nchunks;
 };
 constexpr int kRouteChunk = 64;  // complete blocks per router workgroup
+
+// The hierarchical indexer's block scores (hisa.hip).
+struct HisaArgs {
+  const uint16_t *keys;
+  const uint16_t *q;
+  const float *w;
+  const int32_t *q_seq;
+  const int32_t *q_pos;
+  const float *pooled;     // [S][Mmax][128]
+  const int32_t *heads;    // [T][nh] routed heads, or nullptr = all H heads
+  float *bscore;           // [T][Mmax]: block scores, -inf past the query's blocks
+  int32_t *mt;             // [T]: the query's block count floor(p/B) + 1
+  int S, Lmax, T, H, nh, B, Mmax, nchunks;
+};
+hipError_t launch_hisa_blocks(const HisaArgs &a, hipStream_t st);
+hipError_t launch_hisa_expand(const int32_t *kept, const int32_t *q_pos, int T, int m, int B,
+                              int32_t *cand, hipStream_t st);
 hipError_t launch_route(const RouteArgs &a, hipStream_t st);
 // many queries of one sequence, H <= 64: one kernel, heads written directly
 hipError_t launch_route_tile(const RouteArgs &a, hipStream_t st);

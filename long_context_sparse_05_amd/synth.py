@@ -183,12 +183,21 @@ WORKLOADS = {
         kind="dagger", S=16, L=131072, H=64, B=128, h=8, kc=8192, k=2048),
     "misa_prefill_chunk_4096q_L65536": dict(
         kind="prefill", L=65536, T=4096, H=32, B=128, h=8, k=2048),
+    # the hierarchical indexer (all heads) and MISA composed with it (the
+    # routed heads in both of its stages), on the MISA decode shape; m = 64
+    # kept blocks of 128 keys = 8192 candidate tokens per query
+    "hisa_decode_16x128K": dict(
+        kind="hisa", S=16, L=131072, H=64, queries_per_seq=1, n_needles=64,
+        B=128, m=64, k=2048),
+    "misa_hisa_decode_16x128K": dict(
+        kind="misa_hisa", S=16, L=131072, H=64, queries_per_seq=1, n_needles=64,
+        B=128, h=8, m=64, k=2048),
 }
 
 
 def make_workload(name, seed=0):
     cfg = WORKLOADS[name]
-    if cfg["kind"] == "decode":
+    if cfg["kind"] in ("decode", "hisa", "misa_hisa"):
         case = decode_case(cfg["S"], cfg["L"], cfg["H"], seed=seed,
                            n_needles=cfg.get("n_needles", 0),
                            queries_per_seq=cfg.get("queries_per_seq", 1))

@@ -63,7 +63,8 @@ def test_workspace_sizes(lib):
     b = batch()
     for op, kw in ((abi.MISA_OP_ROUTE, dict(B=64, h=8)), (abi.MISA_OP_SCORE_TOPK, dict(k=256)),
                    (abi.MISA_OP_DENSE, dict(k=256)), (abi.MISA_OP_RERANK, dict(k=256, kc=1024)),
-                   (abi.MISA_OP_TOPK, dict(k=256)), (abi.MISA_OP_INDEXER, dict(B=64, h=8, k=256))):
+                   (abi.MISA_OP_TOPK, dict(k=256)), (abi.MISA_OP_INDEXER, dict(B=64, h=8, k=256)),
+                   (abi.MISA_OP_HISA, dict(B=64, k=256, kc=16))):
         rc, n = ws_bytes(lib, b, op, **kw)
         assert rc == OK and n > 0 and n % 256 == 0
     # the score workspace holds at least the fp32 score rows
@@ -74,6 +75,10 @@ def test_workspace_sizes(lib):
     assert ws_bytes(lib, b, abi.MISA_OP_DENSE, k=4097)[0] == ERR_SHAPE
     assert ws_bytes(lib, b, abi.MISA_OP_RERANK, k=300, kc=200)[0] == ERR_SHAPE
     assert ws_bytes(lib, b, abi.MISA_OP_ROUTE, B=64, h=65)[0] == ERR_SHAPE
+    assert ws_bytes(lib, b, abi.MISA_OP_HISA, B=64, k=8, kc=0)[0] == ERR_SHAPE
+    assert ws_bytes(lib, b, abi.MISA_OP_HISA, B=64, k=8, kc=65)[0] == ERR_SHAPE
+    # the HISA workspace holds the candidate token lists of the m kept blocks
+    assert ws_bytes(lib, b, abi.MISA_OP_HISA, B=64, k=8, kc=16)[1] >= 4 * 16 * 64 * 4
 
 
 def test_validation_before_any_hip_call(lib):
@@ -129,3 +134,16 @@ def test_validation_before_any_hip_call(lib):
     assert lib.misa_indexer(ctypes.byref(b), F, 64, 9999, 0, 64, F, None, F, None, F, big, None) == ERR_SHAPE
     assert lib.misa_indexer(ctypes.byref(b), F, 64, 8, 3, 64, F, None, F, None, F, big, None) == ERR_SHAPE
     assert lib.misa_indexer(ctypes.byref(b), F, 64, 8, 0, 0, F, None, F, None, F, big, None) == ERR_SHAPE
+    # hierarchical indexer: (b, pooled, B, m, heads, h, k, idx, val, ws, ws_bytes, stream)
+    assert lib.hisa_indexer(ctypes.byref(b), None, 64, 4, None, 0, 8, F, None, F, big, None) == ERR_NULL
+    assert lib.hisa_indexer(ctypes.byref(b), F, 64, 4, None, 0, 8, None, None, F, big, None) == ERR_NULL
+    assert lib.hisa_indexer(ctypes.byref(b), F, 64, 0, None, 0, 8, F, None, F, big, None) == ERR_SHAPE
+    assert lib.hisa_indexer(ctypes.byref(b), F, 64, 65, None, 0, 8, F, None, F, big, None) == ERR_SHAPE
+    assert lib.hisa_indexer(ctypes.byref(b), F, 64, 4, None, 3, 8, F, None, F, big, None) == ERR_SHAPE
+    assert lib.hisa_indexer(ctypes.byref(b), F, 64, 4, F, 0, 8, F, None, F, big, None) == ERR_SHAPE
+    assert lib.hisa_indexer(ctypes.byref(b), F, 64, 4, F, 65, 8, F, None, F, big, None) == ERR_SHAPE
+    assert lib.hisa_indexer(ctypes.byref(b), F, 64, 4, None, 0, 0, F, None, F, big, None) == ERR_SHAPE
+    assert lib.hisa_indexer(ctypes.byref(b), F, 0, 4, None, 0, 8, F, None, F, big, None) == ERR_SHAPE
+    assert lib.hisa_indexer(ctypes.byref(b), F, 64, 4, None, 0, 8, F, None, F, small, None) == ERR_WORKSPACE
+    assert lib.hisa_blocks(ctypes.byref(b), F, 64, 4, None, 0, F, F, F, small, None) == ERR_WORKSPACE
+    assert lib.hisa_blocks(ctypes.byref(b), F, 64, 4, None, 0, F, F, None, big, None) == ERR_NULL

@@ -372,6 +372,104 @@ def test_fidelity_sweep_matches_oracle_selections():
             assert r["recall"] == 1.0 and r["iou"] == 1.0, r
 
 
+# ------------------------------------------------ hierarchical indexer (HISA)
+HISA_CASES = [
+    # S, Lmax, T, H, B, m
+    (2, 3000, 6, 16, 64, 5),
+    (3, 4133, 5, 64, 128, 3),
+    (1, 2500, 9, 32, 16, 40),
+    (2, 1000, 4, 8, 128, 1),
+]
+
+
+def _hisa_heads(case, T, H, h, seed):
+    rng = np.random.default_rng(seed)
+    return np.stack([rng.permutation(H)[:h] for _ in range(T)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("S,Lmax,T,H,B,m", HISA_CASES)
+@pytest.mark.parametrize("routed", [False, True])
+def test_hisa_matches_oracle(S, Lmax, T, H, B, m, routed):
+    """Block scores within fp32 accuracy of the oracle, the kept blocks the
+    top-m of the GPU's own block scores and the oracle's (up to a near-tie),
+    and the selected tokens the oracle's (up to swaps at the k-th score)."""
+    abi = _abi()
+    case = make(S, Lmax, T, H, Lmax % 13)
+    b = upload(case)
+    ob = orc.Batch.from_case(case)
+    heads = _hisa_heads(case, T, H, min(4, H), Lmax) if routed else None
+    th = torch.from_numpy(heads).cuda() if routed else None
+    k = min(200, Lmax)
+    pooled = abi.pool(b, B)
+    gs, gb = abi.hisa_blocks(b, pooled, B, m, heads=th)
+    gs, gb = np_(gs), np_(gb)
+    gi, gv = abi.hisa_indexer(b, pooled, B, m, k, heads=th)
+    gi, gv = np_(gi), np_(gv)
+    o = orc.hisa(ob, B, m, k, heads=heads)
+    osc = orc.scores(ob, heads)
+    for t in range(T):
+        M = int(case["q_pos"][t]) // B + 1
+        ob_s = o["bscore"][t, :M]
+        sb = float(np.mean(np.abs(ob_s))) + 1e-30
+        assert np.all(np.abs(gs[t, :M] - ob_s) <= 1e-4 * (np.abs(ob_s) + sb)), t
+        assert np.all(np.isneginf(gs[t, M:]))
+        assert sorted(x for x in gb[t] if x >= 0) == sorted(x for x in orc.topk_f32(gs[t, :M], m) if x >= 0)
+        same_blocks = set(gb[t]) == set(o["blocks"][t])
+        if not same_blocks:
+            assert parity.head_margin(ob_s, min(m, M)) < 1e-4, (t, gb[t], o["blocks"][t])
+            continue
+        # the refinement: the tokens of the kept blocks, ranked by the indexer
+        n = int(case["q_pos"][t]) + 1
+        allowed = np.zeros(n, bool)
+        for blk in gb[t]:
+            if blk >= 0:
+                allowed[blk * B:min(blk * B + B, n)] = True
+        assert all(allowed[i] for i in gi[t] if i >= 0)
+        nc = int(allowed.sum())
+        masked = np.where(allowed, osc[t, :n], -np.inf)
+        parity.check_set(gi[t], o["idx"][t], lambda i: masked[i], nc, k, parity.row_sbar(osc[t], n))
+        for i, v in zip(gi[t], gv[t]):
+            if i >= 0:
+                assert abs(v - osc[t, i]) <= parity.REL * (abs(osc[t, i]) + parity.row_sbar(osc[t], n))
+
+
+@pytest.mark.parametrize("S,Lmax,T,H,B,m", HISA_CASES[:3])
+def test_hisa_keeping_every_block_is_the_dense_indexer(S, Lmax, T, H, B, m):
+    abi = _abi()
+    case = make(S, Lmax, T, H, 3)
+    b = upload(case)
+    pooled = abi.pool(b, B)
+    M = (Lmax + B - 1) // B
+    k = min(300, Lmax)
+    gi, _ = abi.hisa_indexer(b, pooled, B, M, k)
+    di, _ = abi.indexer_dense(b, k)
+    assert [set(r) for r in np_(gi)] == [set(r) for r in np_(di)]
+
+
+def test_hisa_integer_inputs_bit_exact():
+    """Integer q, keys and w with unit blocks: every block and token score is
+    an exact integer on both sides, so blocks, ties and tokens match the
+    oracle exactly, for all heads and for routed heads."""
+    abi = _abi()
+    S, Lmax, T, H = 2, 700, 5, 16
+    case = synth.random_case(S, Lmax, T, H, seed=4, dist="int")
+    b = upload(case)
+    ob = orc.Batch.from_case(case)
+    pooled = abi.pool(b, 1)
+    for heads in (None, _hisa_heads(case, T, H, 3, 1)):
+        th = torch.from_numpy(heads).cuda() if heads is not None else None
+        for m, k in ((40, 30), (7, 20)):
+            gs, gb = abi.hisa_blocks(b, pooled, 1, m, heads=th)
+            gi, gv = abi.hisa_indexer(b, pooled, 1, m, k, heads=th)
+            o = orc.hisa(ob, 1, m, k, heads=heads)
+            gs, gb, gi, gv = np_(gs), np_(gb), np_(gi), np_(gv)
+            for t in range(T):
+                n = int(case["q_pos"][t]) + 1
+                assert np.array_equal(gs[t, :n].astype(np.float64), o["bscore"][t, :n])
+                assert set(gb[t]) == set(o["blocks"][t])
+                assert set(gi[t]) == set(o["idx"][t])
+
+
 # --------------------------------------------------------------------- rerank
 @pytest.mark.parametrize("S,Lmax,T,H,seed", CASES[:4])
 def test_rerank(S, Lmax, T, H, seed):
