@@ -96,6 +96,26 @@ def decode_case(S, L, H, seed=0, n_needles=0, queries_per_seq=1, d=D,
                 q_seq=q_seq, q_pos=q_pos.astype(np.int32))
 
 
+def clustered_case(S, L, H, seed=0, seg=128, center=1.0, noise=0.5, d=D):
+    """Decode inputs whose keys have segment structure: the sequence is cut
+    into segments of `seg` tokens, each with its own center direction
+    c ~ N(0, center^2/d), and every key is its segment's center plus
+    N(0, noise^2/d) token noise.  One query per sequence at its last position,
+    i.i.d. q and w.  The pages measure the hierarchical indexer on real model
+    activations, which have block-level structure that i.i.d. keys lack; this
+    recipe (a reading: the pages give no synthetic model of it) stands in
+    for that structure when the selection fidelity is swept."""
+    r_q, r_k, r_w, _, _ = _streams(seed)
+    nseg = (L + seg - 1) // seg
+    centers = _normal_f32(r_k, (S, nseg, d), center / np.sqrt(d))
+    keys = _normal_f32(r_k, (S, L, d), noise / np.sqrt(d))
+    keys += np.repeat(centers, seg, axis=1)[:, :L]
+    q = _normal_f32(r_q, (S, H, d), 1.0 / np.sqrt(d))
+    w = _normal_f32(r_w, (S, H), 1.0 / np.sqrt(H))
+    return dict(keys=to_bf16_bits(keys), seq_lens=np.full(S, L, np.int32), q=to_bf16_bits(q), w=w,
+                q_seq=np.arange(S, dtype=np.int32), q_pos=np.full(S, L - 1, np.int32))
+
+
 def dagger_case(S, L, H, h, k, seed=0, d=D, frac_outside=0.1,
                 a_coef=0.8, b_coef=0.15, n_coef=1.2):
     """MISA-dagger decode input: needles planted so that a share of the dense

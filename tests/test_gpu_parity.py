@@ -357,18 +357,24 @@ def test_fidelity_sweep_matches_oracle_selections():
     from long_context_sparse_05_amd import fidelity
     S, L, H, k = 4, 3000, 16, 100
     case = synth.decode_case(S, L, H, seed=5, n_needles=8)
-    rows = fidelity.sweep(case, k, hs=[1, 4, H], kps=[400, L], Bs=[16, 64])
+    rows = fidelity.sweep(case, k, hs=[1, 4, H], kps=[400, L], Bs=[16, 64], ms=[3, 200], hisa_h=4)
     ob = orc.Batch.from_case(case)
     dense, _ = orc.dsa(ob, k)
     for r in rows:
         if r["method"] == "MISA":
             sel = orc.misa(ob, r["B"], r["h"], k)["idx"]
-        else:
+        elif r["method"] == "MISA-dagger":
             sel = orc.misa_dagger(ob, r["B"], r["h"], r["kp"], k)["idx"]
+        elif r["method"] == "HISA":
+            sel = orc.hisa(ob, r["B"], r["kp"] // r["B"], k)["idx"]
+        else:
+            heads, _ = orc.route(ob, r["B"], r["h"])
+            sel = orc.hisa(ob, r["B"], r["kp"] // r["B"], k, heads=heads)["idx"]
         orr, ori = fidelity.set_metrics(sel, dense)
         # a near-tie at the k-th boundary may swap one token of a row
         assert abs(r["recall"] - orr) <= 1.5 / k and abs(r["iou"] - ori) <= 3.0 / k, (r, orr, ori)
-        if r["h"] == H or r["kp"] >= L:
+        full = r["kp"] >= L if r["method"] in ("MISA-dagger", "HISA") else False
+        if (r["method"] in ("MISA", "MISA-dagger") and r["h"] == H) or full:
             assert r["recall"] == 1.0 and r["iou"] == 1.0, r
 
 
