@@ -124,7 +124,7 @@ int score_chunk(int rows, int ncols) {
 // tiling of prefill.hip.  Otherwise each query row streams the keys itself.
 constexpr int kPrefillMinRows = 64;
 bool use_prefill(const misa_batch *b, const int32_t *heads, int h) {
-  return heads && b->S == 1 && b->T >= kPrefillMinRows && prefill_supported(h, b->Lmax);
+  return heads && b->S == 1 && b->T >= kPrefillMinRows && prefill_supported(h, b->Lmax, b->Lmax);
 }
 
 PrefillArgs make_prefill_args(const misa_batch *b, const int32_t *heads, int h, float *scores) {
@@ -141,9 +141,10 @@ PrefillArgs make_prefill_args(const misa_batch *b, const int32_t *heads, int h, 
   p.Lmax = b->Lmax;
   p.T = b->T;
   p.ld = b->Lmax;
-  // about 1024 workgroups: query tiles x key splits of whole key tiles
+  // about one workgroup per compute unit (one fits at a time: its A rows fill
+  // the registers): query tiles x key splits of whole key tiles
   const int nqt = (b->T + prefill_queries_per_wg(h) - 1) / prefill_queries_per_wg(h);
-  const int nsplit = std::max(1, std::min((b->Lmax + 1023) / 1024, (1024 + nqt - 1) / nqt));
+  const int nsplit = std::max(1, std::min((b->Lmax + 1023) / 1024, (256 + nqt / 2) / nqt));
   int split = (b->Lmax + nsplit - 1) / nsplit;
   p.split = (split + kPrefillKeyTile - 1) / kPrefillKeyTile * kPrefillKeyTile;
   return p;

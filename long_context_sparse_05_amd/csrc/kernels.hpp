@@ -40,7 +40,7 @@ struct PrefillArgs {
 constexpr int kPrefillKeyTile = 128;
 hipError_t launch_score_prefill(const PrefillArgs &a, hipStream_t st);
 int prefill_queries_per_wg(int h);
-bool prefill_supported(int h, int ld);  // the launch shape fits h and the row length
+bool prefill_supported(int h, int ld, int Lmax);  // the launch shape fits h, the row length and the keys
 
 // Per-row top-k selection (topk.hip).
 struct TopkArgs {

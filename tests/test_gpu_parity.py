@@ -630,6 +630,13 @@ PREFILL_CASES = [
     (2500, 130, 32, 16, "random"),
     (700, 64, 16, 1, "tail"),
     (4200, 256, 64, 8, "tail"),
+    # whole query tiles and key tiles only (no ragged workgroup)
+    (4096, 128, 32, 8, "tail"),
+    (2048, 128, 16, 4, "random"),
+    (2560, 256, 8, 2, "tail"),
+    # ragged only in the keys, or only in the queries
+    (3000, 128, 32, 8, "tail"),
+    (2048, 100, 32, 4, "tail"),
 ]
 
 
