@@ -21,7 +21,7 @@ struct ScoreArgs {
   int nh, H, Lmax, T;
   int ncols, ld, chunk;
 };
-constexpr int kMaxScoreChunk = 4096;  // columns per workgroup of score_rows_kernel (gathered rows)
+constexpr int kMaxScoreChunk = 4096;  // columns per workgroup of score_rows_kernel
 hipError_t launch_score_rows(const ScoreArgs &a, hipStream_t st);
 
 // Routed scoring of many queries of one sequence (prefill.hip).

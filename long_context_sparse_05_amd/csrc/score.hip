@@ -18,9 +18,11 @@
 // weighted ReLU and the head reduction run on the accumulators in registers
 // (four rows per lane), then a reduce-scatter across the four lane groups
 // leaves each group the whole sums of one tile, so a wave stores the scores
-// of 64 (or 32) consecutive columns at once.  The epilogue also builds a
-// 4096-bin histogram of the top 12 bits of each score's order key, the first
-// radix digit of the per-row top-k.
+// of 32 consecutive columns at once.  The scores of the workgroup's chunk
+// collect in LDS and leave in one burst of 16-byte stores at the end: score
+// stores spread through the key stream cost more HBM time than their bytes.
+// The epilogue also builds a 4096-bin histogram of the top 12 bits of each
+// score's order key, the first radix digit of the per-row top-k.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -33,6 +35,7 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
   __shared__ uint32_t lds_hist[kHistBins];
   __shared__ uint4 tile[4][16 * kKeyRowLds / 16];
   __shared__ int32_t ctok[GATHER ? kMaxScoreChunk : 1];  // the chunk's candidate tokens
+  __shared__ float csc[kMaxScoreChunk];                   // the chunk's scores
   const int t = blockIdx.y;
   const int lane = lane_id();
   // wave-uniform, and known to be: the step loop below branches on scalars
@@ -56,31 +59,37 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
     return;
   }
 
-  // Query head fragments (A operand) and the weights of this lane's rows.
+  // Query head fragments (A operand) and the weights of this lane's rows:
+  // two batched rounds of loads (head ids, then rows and weights), indices
+  // clamped and rows past nh masked, so that no load waits behind a branch
   const size_t seq_base = (size_t)a.q_seq[t] * a.Lmax;
   bf16x8 qa[HT][4];
   float wv[HT][4];
+  {
+    int jq[HT], jw[HT][4];
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const int m = ht * 16 + col;
-    int j = -1;
-    if (m < a.nh) j = a.heads ? a.heads[(size_t)t * a.nh + m] : m;
+    for (int ht = 0; ht < HT; ++ht) {
+      const int m = min(ht * 16 + col, a.nh - 1);
+      jq[ht] = a.heads ? a.heads[(size_t)t * a.nh + m] : m;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (j >= 0)
-        v = *(const uint4 *)(a.q + ((size_t)t * a.H + j) * kD + s * 32 + grp * 8);
-      qa[ht][s] = as_bf16x8(v);
+      for (int r = 0; r < 4; ++r) {
+        const int mr = min(ht * 16 + grp * 4 + r, a.nh - 1);
+        jw[ht][r] = a.heads ? a.heads[(size_t)t * a.nh + mr] : mr;
+      }
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int mr = ht * 16 + grp * 4 + r;
-      float wr = 0.f;
-      if (mr < a.nh) {
-        const int jr = a.heads ? a.heads[(size_t)t * a.nh + mr] : mr;
-        wr = a.w[(size_t)t * a.H + jr];
+    for (int ht = 0; ht < HT; ++ht) {
+      const uint32_t mq = ht * 16 + col < a.nh ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 v = *(const uint4 *)(a.q + ((size_t)t * a.H + jq[ht]) * kD + s * 32 + grp * 8);
+        qa[ht][s] = as_bf16x8(make_uint4(v.x & mq, v.y & mq, v.z & mq, v.w & mq));
       }
-      wv[ht][r] = wr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t wb = __float_as_uint(a.w[(size_t)t * a.H + jw[ht][r]]);
+        wv[ht][r] = __uint_as_float(wb & (ht * 16 + grp * 4 + r < a.nh ? 0xFFFFFFFFu : 0u));
+      }
     }
   }
   const int32_t *crow = GATHER ? a.cand + (size_t)t * a.ncols : nullptr;
@@ -133,26 +142,17 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
       }
     }
     // reduce-scatter over the four lane groups (each holds four head rows):
-    // afterwards group g holds the whole sum of tile g (U == 4) or of tile
-    // g / 2 (U == 2), so one store covers U * 16 consecutive columns
-    float own;
-    if constexpr (U == 4) {
-      const bool lo = grp < 2;
-      const float x0 = (lo ? part[0] : part[2]) + __shfl_xor(lo ? part[2] : part[0], 32, kWave);
-      const float x1 = (lo ? part[1] : part[3]) + __shfl_xor(lo ? part[3] : part[1], 32, kWave);
-      const bool ev = (grp & 1) == 0;
-      own = (ev ? x0 : x1) + __shfl_xor(ev ? x1 : x0, 16, kWave);
-    } else {
-      static_assert(U == 2, "two or four tiles per step");
-      const bool lo = grp < 2;
-      own = (lo ? part[0] : part[1]) + __shfl_xor(lo ? part[1] : part[0], 32, kWave);
-      own += __shfl_xor(own, 16, kWave);
-    }
-    const int c = base + (U == 4 ? grp : grp >> 1) * 16 + col;
-    if ((U == 4 || (grp & 1) == 0) && c < c1) {
+    // afterwards groups 0 and 1 hold the whole sum of tile 0, groups 2 and 3
+    // that of tile 1, so one LDS store covers 32 consecutive columns
+    static_assert(U == 2, "two tiles per step");
+    const bool lo = grp < 2;
+    float own = (lo ? part[0] : part[1]) + __shfl_xor(lo ? part[1] : part[0], 32, kWave);
+    own += __shfl_xor(own, 16, kWave);
+    const int c = base + (grp >> 1) * 16 + col;
+    if ((grp & 1) == 0 && c < c1) {
       const bool ok = c < nvalid && (!GATHER || ctok[c - c0] >= 0);
       const float sc = ok ? own : -INFINITY;
-      srow[c] = sc;
+      csc[c - c0] = sc;
       if (hist && ok) atomicAdd(&lds_hist[order_key(sc) >> kHistShift], 1u);
     }
   };
@@ -183,6 +183,19 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
       process_step(b0 + stride, kb2);
     }
   }
+  // the chunk's scores, in 16-byte non-temporal stores where aligned
+  __syncthreads();
+  {
+    const int n = c1 - c0;
+    if ((n & 3) == 0 && (((size_t)t * a.ld + c0) & 3) == 0) {
+      for (int i = threadIdx.x * 4; i < n; i += 1024) {
+        const float4 v = *(const float4 *)&csc[i];
+        __builtin_nontemporal_store((f32x4){v.x, v.y, v.z, v.w}, (f32x4 *)(srow + c0 + i));
+      }
+    } else {
+      for (int i = threadIdx.x; i < n; i += 256) srow[c0 + i] = csc[i];
+    }
+  }
   if (hist) {
     __syncthreads();
     uint32_t *grow = a.hist + (size_t)t * kHistBins;
@@ -196,10 +209,9 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
 template <int HT, bool GATHER>
 static hipError_t launch_ht(const ScoreArgs &a, hipStream_t st) {
   dim3 grid((a.ncols + a.chunk - 1) / a.chunk, a.T);
-  // four 16-key tiles per step (one coalesced 256-byte score store per
-  // wave) where the query fragments leave room in registers, else two
-  constexpr int U = HT <= 2 ? 4 : 2;
-  if (GATHER && a.chunk > kMaxScoreChunk) return hipErrorInvalidValue;
+  // two 16-key tiles per wave step: fewer registers, more waves per CU
+  constexpr int U = 2;
+  if (a.chunk > kMaxScoreChunk) return hipErrorInvalidValue;
   hipLaunchKernelGGL((score_rows_kernel<HT, GATHER, U>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
