@@ -194,7 +194,16 @@ int run_select(const ScoreArgs *score, const float *scores_in, int rows, int ld,
     if (e == hipSuccess && ev_stop) e = hipEventRecord((hipEvent_t)ev_stop, st);
     if (e != hipSuccess) return MISA_ERR_HIP;
   }
-  if (row_mode) return hip_status(launch_topk_rowselect(t, st));
+  if (row_mode) {
+    // many long rows without a column map: the streamed select, then the
+    // register-resident select on the rows it could not settle
+    if (rows >= kRowSelectMinRows && !map && ld % 4 == 0 && ld >= kStreamSelectMinCols &&
+        ld <= kStreamSelectMaxCols && (size_t)k * 8 <= (size_t)ld) {
+      if ((e = launch_topk_stream(t, st)) != hipSuccess) return MISA_ERR_HIP;
+      t.only_flagged = 1;
+    }
+    return hip_status(launch_topk_rowselect(t, st));
+  }
   if (!score) {
     t.chunk = hist_chunk(rows, ld);
     if ((e = launch_topk_hist(t, hist, st)) != hipSuccess) return MISA_ERR_HIP;

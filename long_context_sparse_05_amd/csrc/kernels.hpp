@@ -55,10 +55,14 @@ struct TopkArgs {
   int32_t *idx;            // [rows][k]
   float *val;              // [rows][k] or nullptr
   int rows, ld, k, chunk;  // chunk: columns per workgroup (histogram / filter)
+  int only_flagged;        // row select: skip rows whose counter 7 is 0 (streamed select done)
 };
 hipError_t launch_topk_hist(const TopkArgs &a, uint32_t *hist, hipStream_t st);
 hipError_t launch_topk_select(const TopkArgs &a, hipStream_t st);
 hipError_t launch_topk_rowselect(const TopkArgs &a, hipStream_t st);
+hipError_t launch_topk_stream(const TopkArgs &a, hipStream_t st);  // then the row select on flagged rows
+constexpr int kStreamSelectMinCols = 16384;   // rows of kStreamSelectMinCols..kStreamSelectMaxCols
+constexpr int kStreamSelectMaxCols = 131072;  // columns take the streamed select
 hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t st);
 
 // Block mean-pool (pool.hip).

@@ -23,6 +23,8 @@
 //     crossing digit and compacting the survivors, until the crossing bin
 //     holds exactly the keys still needed.  More than 16384 candidates
 //     (heavy ties) are re-read from the score row instead.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "select.hpp"
@@ -451,7 +453,7 @@ __device__ __forceinline__ bool sample_collect(const TopkArgs &a, int n,
 // The ranking of the candidates sample_collect left in LDS (thread t's
 // slots j < cnt at j*NT + t).  The row's registers are dead here: this is
 // entered only when the collection succeeded, and the kernel ends after it.
-__device__ __forceinline__ void sample_finish(const TopkArgs &a, int n, uint32_t kk, uint32_t tau,
+__device__ __forceinline__ void sample_finish(const TopkArgs &a, int r, int n, uint32_t kk, uint32_t tau,
                                               uint32_t cnt, uint64_t *cs, uint64_t *cs2,
                                               uint32_t *hs, uint32_t *sh) {
   constexpr int NT = kSelThreads;
@@ -480,8 +482,8 @@ __device__ __forceinline__ void sample_finish(const TopkArgs &a, int n, uint32_t
   }
   kmax = wave_max_u32(kmax);
   if (lane_id() == 0 && kmax) atomicMax(&res[5], kmax);
-  int32_t *irow = a.idx + (size_t)blockIdx.x * a.k;
-  float *vrow = a.val ? a.val + (size_t)blockIdx.x * a.k : nullptr;
+  int32_t *irow = a.idx + (size_t)r * a.k;
+  float *vrow = a.val ? a.val + (size_t)r * a.k : nullptr;
   for (int i = (int)kk + tid; i < a.k; i += NT) {
     irow[i] = -1;
     if (vrow) vrow[i] = -INFINITY;
@@ -541,7 +543,7 @@ __device__ __forceinline__ void sample_finish(const TopkArgs &a, int n, uint32_t
 }
 
 template <bool MAP, bool REG>
-__global__ __launch_bounds__(kSelThreads) void topk_rowselect_kernel(TopkArgs a) {
+__device__ __forceinline__ void rowselect_row(const TopkArgs &a, const int r) {
   constexpr int NT = kSelThreads;
   constexpr int NW = NT / kWave;
   constexpr int U = kSelU;
@@ -554,7 +556,6 @@ __global__ __launch_bounds__(kSelThreads) void topk_rowselect_kernel(TopkArgs a)
   uint32_t *res = sh + NW + 4;   // [0] digit [1] count above it [2] count in it
   __shared__ unsigned long long cnt64;  // (above emitted << 32) | candidates collected
   uint32_t *lh = (uint32_t *)cs;  // pass-1 histogram lives in the candidate array
-  const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int n = row_valid_len(a, r);
   const float *srow = a.scores + (size_t)r * a.ld;
@@ -603,7 +604,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_rowselect_kernel(TopkArgs a)
     if constexpr (!MAP) {
       uint32_t cnt, tau, kk;
       if (sample_collect(a, n, sv, cs, sh, cnt, tau, kk)) {  // uniform
-        sample_finish(a, n, kk, tau, cnt, cs, cs2, hs, sh);
+        sample_finish(a, r, n, kk, tau, cnt, cs, cs2, hs, sh);
         return;
       }
     }
@@ -719,18 +720,366 @@ hipError_t launch_topk_hist(const TopkArgs &a, uint32_t *hist, hipStream_t st) {
   return hipGetLastError();
 }
 
+// One workgroup per row.
+template <bool MAP, bool REG>
+__global__ __launch_bounds__(kSelThreads) void topk_rowselect_kernel(TopkArgs a) {
+  rowselect_row<MAP, REG>(a, blockIdx.x);
+}
+
+// The rows the streamed select left (counter 7 set): a grid of at most 256
+// workgroups walks the rows, so a row it settled costs one flag read. It
+// takes the streamed (register-free) form of the row select: wrapped in this
+// loop the register-resident form spills, and the rows that come here are
+// few.
+__global__ __launch_bounds__(kSelThreads) void topk_flagged_kernel(TopkArgs a) {
+  // this workgroup's rows r = blockIdx.x + i * gridDim.x, their flags read
+  // 1024 at a time in one round of loads
+  __shared__ uint32_t fl[kSelThreads];
+  for (int i0 = 0; blockIdx.x + i0 * gridDim.x < a.rows; i0 += kSelThreads) {
+    {
+      const int r = blockIdx.x + (i0 + threadIdx.x) * gridDim.x;
+      fl[threadIdx.x] = r < a.rows ? a.counters[(size_t)r * kRowCounters + 7] : 0u;
+    }
+    __syncthreads();
+    for (int i = 0; i < kSelThreads; ++i) {
+      const int r = blockIdx.x + (i0 + i) * gridDim.x;
+      if (r >= a.rows) break;
+      if (fl[i] == 0u) continue;  // uniform
+      rowselect_row<false, false>(a, r);
+      __syncthreads();  // the next row reuses the LDS
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------ streamed select
+// Many long rows (the score rows of a prefill chunk): one 256-thread
+// workgroup per row, several rows per CU at once, each row read from HBM
+// once (the register-resident row select holds one row per CU and cannot
+// overlap a row's ranking with the next row's loads).
+//  1. A 4096-score sample -- 16 windows of 256 columns spread over the row --
+//     brackets the k-th largest key: with m = kk 4096 / n, tau_lo is the
+//     lower edge of the histogram bin holding the sample's
+//     (m + 4 sqrt(m) + 4)-th largest key and tau_hi the upper edge of the
+//     bin holding its (m - 4 sqrt(m) - 4)-th (a 1024-bin histogram over the
+//     sample's own key range, its crossing bins split again into 1024).
+//  2. One streamed pass (float4 loads, the next round's in flight) appends
+//     the columns with key >= tau_lo to an LDS list of composite keys (key
+//     relative to tau_lo << 32 | ~column; positions from a wave scan and one
+//     LDS atomic per wave and round) and counts those >= tau_hi.
+//  3. If no more than kk columns lie at or above tau_hi and the list holds
+//     at least kk and fits, the entries >= tau_hi are output and the
+//     kk - above still needed are resolved among the band [tau_lo, tau_hi)
+//     by 10-bit digit passes from the highest bit in use, every key above a
+//     pass's crossing digit emitted, until the crossing digit holds exactly
+//     the keys still needed.  Otherwise nothing is written and the row's
+//     flag (counter 7) is set: the register-resident row select takes it.
+constexpr int kStThreads = 256;
+constexpr int kStCap = 4096;                       // candidates held per row
+constexpr int kStU = 4;                            // float4 per thread per round
+constexpr int kStRound = kStThreads * 4 * kStU;    // 4096 columns
+constexpr int kStMinCols = kStreamSelectMinCols;
+constexpr int kStSample = 4096;
+constexpr int kStBins = 1024;                      // histogram bins (sample, band digits)
+
+__global__ __launch_bounds__(kStThreads) void topk_stream_kernel(TopkArgs a) {
+  constexpr int NT = kStThreads, NW = NT / kWave;
+  __shared__ uint64_t cand[kStCap];
+  __shared__ uint32_t hh[kStBins];
+  __shared__ uint32_t sh[NW + 16];
+  __shared__ uint32_t ctr[2];  // [0] candidates appended [1] output slots used
+  const int r = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int n = row_valid_len(a, r);
+  const float *srow = a.scores + (size_t)r * a.ld;
+  uint32_t *flag = a.counters + (size_t)r * kRowCounters + 7;
+  int32_t *irow = a.idx + (size_t)r * a.k;
+  float *vrow = a.val ? a.val + (size_t)r * a.k : nullptr;
+  const uint32_t kk = (uint32_t)min(a.k, n);
+  if (n < kStMinCols || kk == 0) {  // uniform: the exact select takes the row
+    if (tid == 0) *flag = 1u;
+    return;
+  }
+  // The bin of an NB-bin histogram in hh where the count from the top
+  // crosses `need` (need <= the histogram's total), the count above it and
+  // the bin's own count, to sh[NW..NW+2].  Uniform control flow.
+  auto crossing = [&](uint32_t need, auto nb) {
+    constexpr int NB = decltype(nb)::value;
+    constexpr int PER = NB / NT;
+    const int top = NB - 1 - PER * tid;
+    uint32_t v[PER], sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      v[i] = hh[top - i];
+      sum += v[i];
+    }
+    uint32_t total;
+    const uint32_t incl = block_scan<NT>(sum, sh, total), excl = incl - sum;
+    if (excl < need && need <= incl) {
+      uint32_t cum = excl;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        if (cum + v[i] >= need) {
+          sh[NW] = (uint32_t)(top - i);
+          sh[NW + 1] = cum;
+          sh[NW + 2] = v[i];
+          break;
+        }
+        cum += v[i];
+      }
+    }
+    __syncthreads();
+  };
+  using BBIG = std::integral_constant<int, kStBins>;
+
+  // 1. the sample: thread t reads 16 consecutive columns of window t / 16
+  uint32_t skey[16];
+  {
+    const int wbase = (int)(((long long)(tid >> 4) * (n - 256)) / 15) & ~3;
+    const int cs = wbase + (tid & 15) * 16;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 x = *(const float4 *)(srow + cs + 4 * u);
+      skey[4 * u + 0] = order_key(x.x);
+      skey[4 * u + 1] = order_key(x.y);
+      skey[4 * u + 2] = order_key(x.z);
+      skey[4 * u + 3] = order_key(x.w);
+    }
+  }
+  const float m = (float)kk * (float)kStSample / (float)n;
+  const float marg = 4.f * sqrtf(m) + 4.f;
+  const uint32_t rs_lo = (uint32_t)ceilf(m + marg);   // rank of tau_lo in the sample
+  const int rs_hi = (int)floorf(m - marg);            // rank of tau_hi (none if < 1)
+  if (rs_lo >= (uint32_t)kStSample) {
+    if (tid == 0) *flag = 1u;
+    return;
+  }
+  // one histogram of the sample over its own key range, kStBins bins of
+  // 2^s keys: tau_lo = the lower edge of the bin holding the rs_lo-th
+  // largest sample key, tau_hi = the upper edge of the bin of the rs_hi-th
+  uint32_t kmin = ~0u, kmax = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    kmin = min(kmin, skey[e]);
+    kmax = max(kmax, skey[e]);
+  }
+  kmax = wave_max_u32(kmax);
+  kmin = ~wave_max_u32(~kmin);
+  if (lane == 0) {
+    sh[wave] = kmax;
+    sh[NW + 8 + wave] = kmin;
+  }
+  for (int i = tid; i < kStBins; i += NT) hh[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    kmax = max(kmax, sh[i]);
+    kmin = min(kmin, sh[NW + 8 + i]);
+  }
+  kmax = __builtin_amdgcn_readfirstlane(kmax);
+  kmin = __builtin_amdgcn_readfirstlane(kmin);
+  const int rbits = kmax > kmin ? 32 - (int)__clz(kmax - kmin) : 0;
+  const int s1 = max(0, rbits - 10), s2 = max(0, s1 - 10);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) atomicAdd(&hh[(skey[e] - kmin) >> s1], 1u);
+  __syncthreads();
+  crossing(rs_lo, BBIG{});
+  const uint32_t blo = __builtin_amdgcn_readfirstlane(sh[NW]);
+  const uint32_t alo = __builtin_amdgcn_readfirstlane(sh[NW + 1]);
+  __syncthreads();
+  uint32_t bhi = 0, ahi = 0;
+  if (rs_hi >= 1) {
+    crossing((uint32_t)rs_hi, BBIG{});
+    bhi = __builtin_amdgcn_readfirstlane(sh[NW]);
+    ahi = __builtin_amdgcn_readfirstlane(sh[NW + 1]);
+  }
+  // the first level's bins are coarse where the range spans many octaves:
+  // the crossing bins are split again into kStBins sub-bins of 2^s2 keys
+  auto refine = [&](uint32_t b1, uint32_t rank) -> uint32_t {
+    __syncthreads();
+    for (int i = tid; i < kStBins; i += NT) hh[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const uint32_t d = skey[e] - kmin;
+      if ((d >> s1) == b1) atomicAdd(&hh[(d - (b1 << s1)) >> s2], 1u);
+    }
+    __syncthreads();
+    crossing(rank, BBIG{});
+    const uint32_t b2 = __builtin_amdgcn_readfirstlane(sh[NW]);
+    __syncthreads();
+    return b2;
+  };
+  const uint32_t tau_lo = kmin + (blo << s1) + (refine(blo, rs_lo - alo) << s2);
+  uint64_t tau_hi = 1ull << 32;  // keys >= tau_hi rank in the top kk when no more than kk lie there
+  if (rs_hi >= 1)
+    tau_hi = (uint64_t)kmin + ((uint64_t)bhi << s1) + ((uint64_t)(refine(bhi, (uint32_t)rs_hi - ahi) + 1) << s2);
+  if (tid == 0) {
+    ctr[0] = 0;
+    ctr[1] = 0;
+  }
+  __syncthreads();
+
+  // 2. the streamed pass
+  auto load_round = [&](int base, float4 (&v)[kStU]) {
+#pragma unroll
+    for (int u = 0; u < kStU; ++u) {
+      const uint32_t cf = (uint32_t)min(base + u * NT * 4 + 4 * tid, a.ld - 4);
+      v[u] = *(const float4 *)((const char *)srow + cf * 4u);
+    }
+  };
+  uint32_t nhi = 0;  // this thread's columns above tau_hi
+  auto scan_round = [&](int base, const float4 (&v)[kStU]) {
+    uint32_t bits = 0;
+#pragma unroll
+    for (int u = 0; u < kStU; ++u) {
+      const float x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = base + u * NT * 4 + 4 * tid + e;
+        const uint32_t key = order_key(x[e]);
+        const bool ok = c < n && key >= tau_lo;
+        nhi += (ok && (uint64_t)key >= tau_hi) ? 1u : 0u;
+        bits |= (ok ? 1u : 0u) << (u * 4 + e);
+      }
+    }
+    const uint32_t mine = (uint32_t)__popc(bits);
+    const uint32_t incl = wave_incl_scan(mine);
+    const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+    uint32_t wb = 0;
+    if (lane == kWave - 1 && wtot) wb = atomicAdd(&ctr[0], wtot);
+    uint32_t pos = (uint32_t)__builtin_amdgcn_readlane((int)wb, kWave - 1) + incl - mine;
+#pragma unroll
+    for (int u = 0; u < kStU; ++u) {
+      const float x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if ((bits >> (u * 4 + e)) & 1u) {
+          if (pos < (uint32_t)kStCap) cand[pos] = composite(order_key(x[e]) - tau_lo, base + u * NT * 4 + 4 * tid + e);
+          ++pos;
+        }
+      }
+    }
+  };
+  {
+    float4 va[kStU], vb[kStU];
+    load_round(0, va);
+    for (int base = 0;; base += 2 * kStRound) {
+      load_round(base + kStRound, vb);
+      scan_round(base, va);
+      if (base + kStRound >= n) break;
+      load_round(base + 2 * kStRound, va);
+      scan_round(base + kStRound, vb);
+      if (base + 2 * kStRound >= n) break;
+    }
+  }
+  uint32_t nh_total;
+  block_scan<NT>(nhi, sh, nh_total);
+  const uint32_t nabove = __builtin_amdgcn_readfirstlane(nh_total);
+  const uint32_t total = __builtin_amdgcn_readfirstlane(ctr[0]);
+  if (nabove > kk || total > (uint32_t)kStCap || total < kk) {  // uniform
+    // (the flag names the reason: 2 too many above tau_hi, 3 the list
+    // overflowed, 4 too few at or above tau_lo; 1 is a row this select does
+    // not take)
+    if (tid == 0) *flag = nabove > kk ? 2u : total > (uint32_t)kStCap ? 3u : 4u;
+    return;
+  }
+  if (tid == 0) *flag = 0u;
+  // list entries at or above tau_hi (relative key >= hib) are in (they leave
+  // with the first band pass's emissions); the band below supplies the
+  // kk - nabove still needed
+  const uint64_t hib = tau_hi >= (1ull << 32) ? ~0ull : (tau_hi - tau_lo) << 32;
+
+  // 3. the kk - nabove best of the band: 10-bit digit passes
+  uint32_t need = kk - nabove;
+  if (need == 0) {
+    for (uint32_t i0 = 0; i0 < total; i0 += NT) {
+      const uint32_t i = i0 + tid;
+      const uint64_t x = i < total ? cand[i] : 0ull;
+      uint32_t pos;
+      if (lds_append(i < total && x >= hib, &ctr[1], pos) && pos < kk) {
+        irow[pos] = (int32_t)~(uint32_t)x;
+        if (vrow) vrow[pos] = key_to_float((uint32_t)(x >> 32) + tau_lo);
+      }
+    }
+  } else {
+    uint32_t hmax = 0;
+    for (uint32_t i = tid; i < total; i += NT)
+      if (cand[i] < hib) hmax = max(hmax, (uint32_t)(cand[i] >> 32));
+    hmax = wave_max_u32(hmax);
+    if (lane == 0) sh[wave] = hmax;
+    __syncthreads();
+    uint32_t top = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) top = max(top, sh[i]);
+    top = __builtin_amdgcn_readfirstlane(top);
+    // the highest bit in use: in the relative key, or else in the column word
+    int shift = top ? 32 + max(0, 31 - (int)__clz(top) - 9) : 22;
+    uint64_t prefix = 0, pmask = 0;
+    for (bool first = true;; first = false) {
+      __syncthreads();
+      for (int i = tid; i < kStBins; i += NT) hh[i] = 0;
+      __syncthreads();
+      for (uint32_t i = tid; i < total; i += NT) {
+        const uint64_t x = cand[i];
+        if (x < hib && (x & pmask) == prefix) atomicAdd(&hh[(uint32_t)(x >> shift) & (kStBins - 1)], 1u);
+      }
+      __syncthreads();
+      crossing(need, BBIG{});
+      const uint32_t b = __builtin_amdgcn_readfirstlane(sh[NW]);
+      const uint32_t above = __builtin_amdgcn_readfirstlane(sh[NW + 1]);
+      const uint32_t inb = __builtin_amdgcn_readfirstlane(sh[NW + 2]);
+      const bool last = inb == need - above;  // the crossing digit holds exactly the keys still needed
+      // every thread visits the same number of list slots, so the wave-level
+      // appends inside run with all lanes present
+      for (uint32_t i0 = 0; i0 < total; i0 += NT) {
+        const uint32_t i = i0 + tid;
+        const uint64_t x = i < total ? cand[i] : 0ull;
+        const uint32_t d = (uint32_t)(x >> shift) & (kStBins - 1);
+        const bool out = i < total && (x < hib ? (x & pmask) == prefix && (d > b || (last && d == b)) : first);
+        uint32_t pos;
+        if (lds_append(out, &ctr[1], pos) && pos < kk) {
+          irow[pos] = (int32_t)~(uint32_t)x;
+          if (vrow) vrow[pos] = key_to_float((uint32_t)(x >> 32) + tau_lo);
+        }
+      }
+      if (last) break;
+      need -= above;
+      prefix |= (uint64_t)b << shift;
+      pmask |= (uint64_t)(kStBins - 1) << shift;
+      shift = max(shift - 10, 0);
+    }
+  }
+  for (int i = (int)kk + tid; i < a.k; i += NT) {
+    irow[i] = -1;
+    if (vrow) vrow[i] = -INFINITY;
+  }
+}
+
+hipError_t launch_topk_stream(const TopkArgs &a, hipStream_t st) {
+  if (a.map || a.ld % 4 || a.ld < kStMinCols) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_stream_kernel, dim3(a.rows), dim3(kStThreads), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk_rowselect(const TopkArgs &a, hipStream_t st) {
+  if (a.only_flagged) {
+    if (a.map) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(topk_flagged_kernel, dim3(a.rows < 256 ? a.rows : 256), dim3(kSelThreads), 0,
+                       st, a);
+    return hipGetLastError();
+  }
   const bool reg = a.ld <= kRegCols && a.ld % 4 == 0;
+  const dim3 grid(a.rows);
   if (a.map) {
     if (reg)
-      hipLaunchKernelGGL((topk_rowselect_kernel<true, true>), dim3(a.rows), dim3(kSelThreads), 0, st, a);
+      hipLaunchKernelGGL((topk_rowselect_kernel<true, true>), grid, dim3(kSelThreads), 0, st, a);
     else
-      hipLaunchKernelGGL((topk_rowselect_kernel<true, false>), dim3(a.rows), dim3(kSelThreads), 0, st, a);
+      hipLaunchKernelGGL((topk_rowselect_kernel<true, false>), grid, dim3(kSelThreads), 0, st, a);
   } else {
     if (reg)
-      hipLaunchKernelGGL((topk_rowselect_kernel<false, true>), dim3(a.rows), dim3(kSelThreads), 0, st, a);
+      hipLaunchKernelGGL((topk_rowselect_kernel<false, true>), grid, dim3(kSelThreads), 0, st, a);
     else
-      hipLaunchKernelGGL((topk_rowselect_kernel<false, false>), dim3(a.rows), dim3(kSelThreads), 0, st, a);
+      hipLaunchKernelGGL((topk_rowselect_kernel<false, false>), grid, dim3(kSelThreads), 0, st, a);
   }
   return hipGetLastError();
 }

@@ -192,6 +192,32 @@ def test_topk_row_mode_long_rows(ld, k):
         assert np.all(idx[r][idx[r] >= 0] < n)
 
 
+@pytest.mark.parametrize("k", [1, 300, 2048, 4096])
+def test_topk_streamed_select(k):
+    """Many long rows take the streamed select (sampled threshold, one pass,
+    the list resolved in LDS); rows it cannot settle -- prefixes too short,
+    heavy ties, a list above its capacity (k = 4096 here) -- go to the
+    register-resident select.  Every row is checked exactly."""
+    abi = _abi()
+    rows, ld = 512, 32768
+    rng = np.random.default_rng(k + 7)
+    kinds = ["normal", "needles", "ramp", "ties", "mod4_hi"]
+    v = np.concatenate([_skewed_rows(rng, (rows + 4) // 5, ld, kd) for kd in kinds])[:rows]
+    v[5::11] = _topk_rows(rng, len(v[5::11]), ld, "spread")
+    v[6::13] = _topk_rows(rng, len(v[6::13]), ld, "ties")
+    row_len = np.full(rows, ld, np.int32)
+    row_len[1::3] = rng.integers(0, ld + 1, size=len(row_len[1::3]))  # some below the streamed minimum
+    row_len[2] = 16384
+    row_len[3] = 16383
+    row_len[4] = min(ld, k)
+    idx, val = abi.topk(torch.from_numpy(v).cuda(), torch.from_numpy(row_len).cuda(), k)
+    idx, val = np_(idx), np_(val)
+    for r in range(rows):
+        n = int(row_len[r])
+        parity.check_exact_topk(idx[r], val[r], v[r], n, k, orc.topk_f32)
+        assert np.all(idx[r][idx[r] >= 0] < n)
+
+
 # ---------------------------------------------------------- score + top-k
 @pytest.mark.parametrize("S,Lmax,T,H,seed", CASES)
 @pytest.mark.parametrize("k", [1, 64, 600])
