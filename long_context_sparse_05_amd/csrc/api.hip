@@ -197,7 +197,8 @@ int run_select(const ScoreArgs *score, const float *scores_in, int rows, int ld,
   if (row_mode) {
     // many long rows without a column map: the streamed select, then the
     // register-resident select on the rows it could not settle
-    if (rows >= kRowSelectMinRows && !map && ld % 4 == 0 && ld >= kStreamSelectMinCols &&
+    if (rows >= kRowSelectMinRows && !map && ld % 4 == 0 && ((uintptr_t)t.scores & 15) == 0 &&
+        ld >= kStreamSelectMinCols &&
         ld <= kStreamSelectMaxCols && (size_t)k * 8 <= (size_t)ld) {
       if ((e = launch_topk_stream(t, st)) != hipSuccess) return MISA_ERR_HIP;
       t.only_flagged = 1;

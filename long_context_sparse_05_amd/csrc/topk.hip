@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a) {
   const int c0 = blockIdx.x * a.chunk, c1 = min(c0 + a.chunk, n);
   const float *srow = a.scores + (size_t)r * a.ld;
   const int32_t *mrow = MAP ? a.map + (size_t)r * a.ld : nullptr;
-  const bool vec = (a.ld % 4) == 0;  // 16-byte aligned rows
+  const bool vec = (a.ld % 4) == 0 && ((uintptr_t)a.scores & 15) == 0;  // 16-byte aligned rows
 
   auto load_round = [&](int sb, float (&sv)[4][4]) {
 #pragma unroll
@@ -560,7 +560,7 @@ __device__ __forceinline__ void rowselect_row(const TopkArgs &a, const int r) {
   const int n = row_valid_len(a, r);
   const float *srow = a.scores + (size_t)r * a.ld;
   const int32_t *mrow = MAP ? a.map + (size_t)r * a.ld : nullptr;
-  const bool vec = (a.ld % 4) == 0;
+  const bool vec = (a.ld % 4) == 0 && ((uintptr_t)a.scores & 15) == 0;  // 16-byte aligned rows
 
   auto load_round = [&](int base, float (&sv)[U][4]) {
 #pragma unroll
@@ -1056,7 +1056,7 @@ __global__ __launch_bounds__(kStThreads) void topk_stream_kernel(TopkArgs a) {
 }
 
 hipError_t launch_topk_stream(const TopkArgs &a, hipStream_t st) {
-  if (a.map || a.ld % 4 || a.ld < kStMinCols) return hipErrorInvalidValue;
+  if (a.map || a.ld % 4 || ((uintptr_t)a.scores & 15) || a.ld < kStMinCols) return hipErrorInvalidValue;
   hipLaunchKernelGGL(topk_stream_kernel, dim3(a.rows), dim3(kStThreads), 0, st, a);
   return hipGetLastError();
 }
@@ -1068,7 +1068,8 @@ hipError_t launch_topk_rowselect(const TopkArgs &a, hipStream_t st) {
                        st, a);
     return hipGetLastError();
   }
-  const bool reg = a.ld <= kRegCols && a.ld % 4 == 0;
+  // the register-resident form reads 16-byte vectors
+  const bool reg = a.ld <= kRegCols && a.ld % 4 == 0 && ((uintptr_t)a.scores & 15) == 0;
   const dim3 grid(a.rows);
   if (a.map) {
     if (reg)

@@ -218,6 +218,62 @@ def test_topk_streamed_select(k):
         assert np.all(idx[r][idx[r] >= 0] < n)
 
 
+def test_topk_streamed_select_wide_rows_and_infinities():
+    """The streamed select at its widest rows (131072 columns) on value
+    patterns a caller's score rows can hold: -inf tails (a prefix shorter
+    than the row), all -inf, a few +inf, signed zeros around the k-th score
+    (-0 ranks equal to +0, so the lower index wins), values spanning many
+    binades, all-negative rows.  Every row is checked exactly."""
+    abi = _abi()
+    rows, ld, k = 256, 131072, 2048
+    rng = np.random.default_rng(131)
+    v = rng.standard_normal((rows, ld)).astype(np.float32)
+    for r in range(rows):
+        kind = r % 8
+        if kind == 1:                      # -inf tail after a random prefix
+            v[r, rng.integers(k, ld):] = -np.inf
+        elif kind == 2 and r % 16 == 2:    # the whole row -inf
+            v[r, :] = -np.inf
+        elif kind == 3:                    # a few +inf
+            v[r, rng.choice(ld, 5, replace=False)] = np.inf
+        elif kind == 4:                    # signed zeros straddle the k-th score
+            v[r] = np.abs(v[r])
+            z = rng.choice(ld, ld - k // 2, replace=False)
+            v[r, z] = np.where(rng.random(z.size) < 0.5, np.float32(0.0), np.float32(-0.0))
+        elif kind == 5:                    # many binades
+            v[r] = (rng.standard_normal(ld) * 10.0 ** rng.uniform(-30, 30, ld)).astype(np.float32)
+        elif kind == 6:                    # all negative
+            v[r] = -np.abs(v[r]) - 1.0
+    row_len = np.full(rows, ld, np.int32)
+    row_len[7::8] = rng.integers(16384, ld + 1, size=len(row_len[7::8]))
+    idx, val = abi.topk(torch.from_numpy(v).cuda(), torch.from_numpy(row_len).cuda(), k)
+    idx, val = np_(idx), np_(val)
+    for r in range(rows):
+        n = int(row_len[r])
+        parity.check_exact_topk(idx[r], val[r], v[r], n, k, orc.topk_f32)
+        assert np.all(idx[r][idx[r] >= 0] < n)
+
+
+@pytest.mark.parametrize("rows,ld,k", [(300, 32768, 512), (4, 65536, 2048)])
+def test_topk_unaligned_score_rows(rows, ld, k):
+    """Score rows that start 4 bytes past a 16-byte boundary (a view into a
+    larger buffer): the selects read them with scalar loads."""
+    abi = _abi()
+    rng = np.random.default_rng(rows + k)
+    v = rng.standard_normal((rows, ld)).astype(np.float32)
+    row_len = np.full(rows, ld, np.int32)
+    row_len[1::5] = rng.integers(k, ld + 1, size=len(row_len[1::5]))
+    buf = torch.empty(rows * ld + 1, dtype=torch.float32, device="cuda")
+    sc = buf[1:].view(rows, ld)
+    sc.copy_(torch.from_numpy(v))
+    assert sc.data_ptr() % 16 == 4
+    idx, val = abi.topk(sc, torch.from_numpy(row_len).cuda(), k)
+    idx, val = np_(idx), np_(val)
+    for r in range(rows):
+        n = int(row_len[r])
+        parity.check_exact_topk(idx[r], val[r], v[r], n, k, orc.topk_f32)
+
+
 # ---------------------------------------------------------- score + top-k
 @pytest.mark.parametrize("S,Lmax,T,H,seed", CASES)
 @pytest.mark.parametrize("k", [1, 64, 600])
