@@ -763,10 +763,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_flagged_kernel(TopkArgs a) {
 //     (m + 4 sqrt(m) + 4)-th largest key and tau_hi the upper edge of the
 //     bin holding its (m - 4 sqrt(m) - 4)-th (a 1024-bin histogram over the
 //     sample's own key range, its crossing bins split again into 1024).
-//  2. One streamed pass (float4 loads, the next round's in flight) appends
-//     the columns with key >= tau_lo to an LDS list of composite keys (key
-//     relative to tau_lo << 32 | ~column; positions from a wave scan and one
-//     LDS atomic per wave and round) and counts those >= tau_hi.
+//  2. One streamed pass (non-temporal 16-byte loads, the next round's in
+//     flight) appends the columns with key >= tau_lo to an LDS list of
+//     composite keys (key relative to tau_lo << 32 | ~column; positions from
+//     a wave scan and one LDS atomic per wave and round) and counts those
+//     >= tau_hi.
 //  3. If no more than kk columns lie at or above tau_hi and the list holds
 //     at least kk and fits, the entries >= tau_hi are output and the
 //     kk - above still needed are resolved among the band [tau_lo, tau_hi)
@@ -924,7 +925,9 @@ __global__ __launch_bounds__(kStThreads) void topk_stream_kernel(TopkArgs a) {
 #pragma unroll
     for (int u = 0; u < kStU; ++u) {
       const uint32_t cf = (uint32_t)min(base + u * NT * 4 + 4 * tid, a.ld - 4);
-      v[u] = *(const float4 *)((const char *)srow + cf * 4u);
+      const uint4 t = load_nt16((const char *)srow + cf * 4u);  // read once
+      v[u] = make_float4(__uint_as_float(t.x), __uint_as_float(t.y), __uint_as_float(t.z),
+                         __uint_as_float(t.w));
     }
   };
   uint32_t nhi = 0;  // this thread's columns above tau_hi
