@@ -308,7 +308,8 @@ def main(argv=None):
         step()
         ev.record(cev[i][1], sp)
     torch.cuda.synchronize()
-    cold_ms = float(np.mean([ev.ms(a, c) for a, c in cev]))
+    cold_all = np.array([ev.ms(a, c) for a, c in cev])
+    cold_ms = float(np.mean(cold_all))
     del flush
     step()  # leave the fused call's outputs for the parity check
     torch.cuda.synchronize()
@@ -359,6 +360,8 @@ def main(argv=None):
                    "queries": int(b.T), "H_I": int(b.H), "B": B, "h": h, "k": k, "d": 128},
         "us_per_batch": ms_step * 1e3,
         "us_per_batch_cold": cold_ms * 1e3,
+        # each cold step bracketed by its own events: median and spread
+        "us_per_batch_cold_p10_p50_p90": [float(np.percentile(cold_all, q)) * 1e3 for q in (10, 50, 90)],
         "score_kernel_us": score_ms * 1e3,
         "wall_s_timed": wall,
         "roofline": roof,
