@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "../../include/misa_indexer.h"
 #include "common.hpp"
@@ -161,6 +162,20 @@ constexpr int kRowSelectMinRows = 256;
 // select kernel beats the fill + histogram + filter + finish chain.
 constexpr int kRowSelectMaxShortRow = 16384;
 
+// The streamed select keeps the columns at or above a sampled bracket of
+// the k-th score in a list of kStreamSelectCap entries per row; a row whose
+// list overflows goes on to the row select.  With m = k * sample / ld, the
+// list holds about r = m + 4 sqrt(m) + 4 sample ranks' worth of columns,
+// r * ld / sample entries with a standard deviation of about
+// sqrt(r) * ld / sample; rows take the streamed select when two standard
+// deviations above the mean still fit (ld is the longest row: shorter rows
+// make smaller lists).
+bool stream_select_fits(int k, int ld) {
+  const double m = (double)k * kStreamSelectSample / ld;
+  const double r = m + 4.0 * std::sqrt(m) + 4.0;
+  return (r + 2.0 * std::sqrt(r)) * ld / kStreamSelectSample <= (double)kStreamSelectCap;
+}
+
 int run_select(const ScoreArgs *score, const float *scores_in, int rows, int ld,
                const int32_t *row_len, int row_len_add, const int32_t *map, int k,
                int32_t *idx, float *val, void *ws, const SelectLayout &L, hipStream_t st,
@@ -198,8 +213,7 @@ int run_select(const ScoreArgs *score, const float *scores_in, int rows, int ld,
     // many long rows without a column map: the streamed select, then the
     // register-resident select on the rows it could not settle
     if (rows >= kRowSelectMinRows && !map && ld % 4 == 0 && ((uintptr_t)t.scores & 15) == 0 &&
-        ld >= kStreamSelectMinCols &&
-        ld <= kStreamSelectMaxCols && (size_t)k * 8 <= (size_t)ld) {
+        ld >= kStreamSelectMinCols && ld <= kStreamSelectMaxCols && stream_select_fits(k, ld)) {
       if ((e = launch_topk_stream(t, st)) != hipSuccess) return MISA_ERR_HIP;
       t.only_flagged = 1;
     }

@@ -63,6 +63,8 @@ hipError_t launch_topk_rowselect(const TopkArgs &a, hipStream_t st);
 hipError_t launch_topk_stream(const TopkArgs &a, hipStream_t st);  // then the row select on flagged rows
 constexpr int kStreamSelectMinCols = 16384;   // rows of kStreamSelectMinCols..kStreamSelectMaxCols
 constexpr int kStreamSelectMaxCols = 131072;  // columns take the streamed select
+constexpr int kStreamSelectCap = 4096;        // its list of bracketed columns, per row
+constexpr int kStreamSelectSample = 4096;     // its sample, per row
 hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t st);
 
 // Block mean-pool (pool.hip).

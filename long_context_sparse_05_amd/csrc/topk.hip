@@ -776,11 +776,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_flagged_kernel(TopkArgs a) {
 //     the keys still needed.  Otherwise nothing is written and the row's
 //     flag (counter 7) is set: the register-resident row select takes it.
 constexpr int kStThreads = 256;
-constexpr int kStCap = 4096;                       // candidates held per row
+constexpr int kStCap = kStreamSelectCap;           // candidates held per row
 constexpr int kStU = 4;                            // float4 per thread per round
 constexpr int kStRound = kStThreads * 4 * kStU;    // 4096 columns
 constexpr int kStMinCols = kStreamSelectMinCols;
-constexpr int kStSample = 4096;
+constexpr int kStSample = kStreamSelectSample;
 constexpr int kStBins = 1024;                      // histogram bins (sample, band digits)
 
 __global__ __launch_bounds__(kStThreads) void topk_stream_kernel(TopkArgs a) {

@@ -196,8 +196,9 @@ def test_topk_row_mode_long_rows(ld, k):
 def test_topk_streamed_select(k):
     """Many long rows take the streamed select (sampled threshold, one pass,
     the list resolved in LDS); rows it cannot settle -- prefixes too short,
-    heavy ties, a list above its capacity (k = 4096 here) -- go to the
-    register-resident select.  Every row is checked exactly."""
+    heavy ties that overflow its list -- go on to the row select, and a k
+    whose expected list does not fit (k = 4096 here) takes the row select
+    alone.  Every row is checked exactly."""
     abi = _abi()
     rows, ld = 512, 32768
     rng = np.random.default_rng(k + 7)
