@@ -279,9 +279,8 @@ def main(argv=None):
     wall = time.perf_counter() - wall0
     ms_step = ev.ms(t_start, t_stop) / K
     # the scoring kernel's own duration: a second pass of K steps with events
-    # recorded on the launch stream right around that kernel (an event
-    # between kernels costs a few microseconds, so it stays out of the
-    # headline region)
+    # attached to that kernel's launch on its stream (the library stamps
+    # them with the kernel's begin and end); kept out of the headline region
     sev = [(ev.create(), ev.create()) for _ in range(K)]
     for i in range(K):
         step(sev[i])

@@ -200,9 +200,11 @@ int misa_score_topk(const misa_batch *b, const int32_t *heads, int32_t h,
 /*
  * misa_score_topk_ev -- misa_score_topk with a measurement hook: ev_start and
  * ev_stop (hipEvent_t passed as void*, created by the caller; either may be
- * NULL) are recorded on `stream` immediately before and after the
- * token-scoring kernel, so hipEventElapsedTime(ev_start, ev_stop) is that
- * kernel's duration.  Everything else is exactly misa_score_topk.
+ * NULL) are attached to the token-scoring kernel launches on `stream`
+ * (hipExtLaunchKernelGGL), which stamp them with the begin of the first and
+ * the end of the last of those kernels, so hipEventElapsedTime(ev_start,
+ * ev_stop) is the scoring kernels' own duration.  Everything else is exactly
+ * misa_score_topk.
  */
 int misa_score_topk_ev(const misa_batch *b, const int32_t *heads, int32_t h,
                        int32_t k, int32_t *idx, float *val, void *ws,
@@ -279,8 +281,9 @@ int hisa_indexer(const misa_batch *b, const float *pooled, int32_t B, int32_t m,
                  const int32_t *heads, int32_t h, int32_t k, int32_t *idx, float *val, void *ws,
                  size_t ws_bytes, void *stream);
 
-/* hisa_indexer with hipEvent_t handles recorded around the token-level
- * scoring kernel (measurement hook; either may be NULL). */
+/* hisa_indexer with the measurement hook of misa_score_topk_ev: the
+ * hipEvent_t handles (either may be NULL) mark the begin and end of the
+ * token-level scoring kernel. */
 int hisa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t m,
                     const int32_t *heads, int32_t h, int32_t k, int32_t *idx, float *val, void *ws,
                     size_t ws_bytes, void *stream, void *ev_start, void *ev_stop);

@@ -204,9 +204,7 @@ int run_select(const ScoreArgs *score, const float *scores_in, int rows, int ld,
   if (score) {
     ScoreArgs s = *score;
     s.hist = row_mode ? nullptr : hist;
-    if (ev_start && hipEventRecord((hipEvent_t)ev_start, st) != hipSuccess) return MISA_ERR_HIP;
-    e = launch_score_rows(s, st);
-    if (e == hipSuccess && ev_stop) e = hipEventRecord((hipEvent_t)ev_stop, st);
+    e = launch_score_rows(s, st, (hipEvent_t)ev_start, (hipEvent_t)ev_stop);
     if (e != hipSuccess) return MISA_ERR_HIP;
   }
   if (row_mode) {
@@ -410,11 +408,8 @@ int misa_score_topk_ev(const misa_batch *b, const int32_t *heads, int32_t h, int
   if (ws_bytes < L.total) return MISA_ERR_WORKSPACE;
   if (use_prefill(b, heads, h)) {
     float *sc = (float *)((char *)ws + L.scores);
-    if (ev_start && hipEventRecord((hipEvent_t)ev_start, (hipStream_t)stream) != hipSuccess)
-      return MISA_ERR_HIP;
-    if (launch_score_prefill(make_prefill_args(b, heads, h, sc), (hipStream_t)stream) != hipSuccess)
-      return MISA_ERR_HIP;
-    if (ev_stop && hipEventRecord((hipEvent_t)ev_stop, (hipStream_t)stream) != hipSuccess)
+    if (launch_score_prefill(make_prefill_args(b, heads, h, sc), (hipStream_t)stream,
+                             (hipEvent_t)ev_start, (hipEvent_t)ev_stop) != hipSuccess)
       return MISA_ERR_HIP;
     return run_select(nullptr, sc, b->T, b->Lmax, b->q_pos, 1, nullptr, k, idx, val, ws, L,
                       (hipStream_t)stream);
@@ -459,11 +454,8 @@ int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t
   if (dispatch_route(b, ra, (hipStream_t)stream, zeroed) != hipSuccess) return MISA_ERR_HIP;
   if (use_prefill(b, heads, h)) {
     float *sc = (float *)((char *)sws + L.scores);
-    if (ev_start && hipEventRecord((hipEvent_t)ev_start, (hipStream_t)stream) != hipSuccess)
-      return MISA_ERR_HIP;
-    if (launch_score_prefill(make_prefill_args(b, heads, h, sc), (hipStream_t)stream) != hipSuccess)
-      return MISA_ERR_HIP;
-    if (ev_stop && hipEventRecord((hipEvent_t)ev_stop, (hipStream_t)stream) != hipSuccess)
+    if (launch_score_prefill(make_prefill_args(b, heads, h, sc), (hipStream_t)stream,
+                             (hipEvent_t)ev_start, (hipEvent_t)ev_stop) != hipSuccess)
       return MISA_ERR_HIP;
     return run_select(nullptr, sc, b->T, b->Lmax, b->q_pos, 1, nullptr, k, idx, val, sws, L,
                       (hipStream_t)stream, nullptr, nullptr, zeroed);

@@ -22,7 +22,11 @@ struct ScoreArgs {
   int ncols, ld, chunk;
 };
 constexpr int kMaxScoreChunk = 4096;  // columns per workgroup of score_rows_kernel
-hipError_t launch_score_rows(const ScoreArgs &a, hipStream_t st);
+// ev0 / ev1 (optional): hipExtLaunchKernelGGL stamps them with the begin of
+// the first and the end of the last kernel a launcher issues, so
+// hipEventElapsedTime(ev0, ev1) is the kernels' own duration.
+hipError_t launch_score_rows(const ScoreArgs &a, hipStream_t st, hipEvent_t ev0 = nullptr,
+                             hipEvent_t ev1 = nullptr);
 
 // Routed scoring of many queries of one sequence (prefill.hip).
 struct PrefillArgs {
@@ -38,7 +42,8 @@ struct PrefillArgs {
 };
 // key tile of the prefill kernel: PrefillArgs::split must be a multiple
 constexpr int kPrefillKeyTile = 128;
-hipError_t launch_score_prefill(const PrefillArgs &a, hipStream_t st);
+hipError_t launch_score_prefill(const PrefillArgs &a, hipStream_t st, hipEvent_t ev0 = nullptr,
+                                hipEvent_t ev1 = nullptr);
 int prefill_queries_per_wg(int h);
 bool prefill_supported(int h, int ld, int Lmax);  // the launch shape fits h, the row length and the keys
 

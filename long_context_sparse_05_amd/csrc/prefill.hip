@@ -36,6 +36,8 @@
 #include <climits>
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -301,7 +303,7 @@ constexpr int kPfWaves = 8, kPfKeys = kPrefillKeyTile;
 constexpr int pf_rt(int hp) { return hp >= 4 ? 2 : 1; }
 
 template <int HP>
-static hipError_t launch_hp(const PrefillArgs &a, hipStream_t st) {
+static hipError_t launch_hp(const PrefillArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   constexpr int RT = pf_rt(HP);
   constexpr int QWG = kPfWaves * RT * (32 / HP);
   if (a.split % kPfKeys) return hipErrorInvalidValue;
@@ -311,15 +313,24 @@ static hipError_t launch_hp(const PrefillArgs &a, hipStream_t st) {
   // whole workgroups: every row a query, every split a whole number of tiles
   const int nq_full = a.T / QWG;
   const int ns_full = (a.Lmax % kPfKeys == 0) ? nsplit : nsplit - 1;
-  if (nq_full > 0 && ns_full > 0)
-    hipLaunchKernelGGL((score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, false>), dim3(ns_full, nq_full),
-                       dim3(kPfWaves * 64), 0, st, a, 0, 0);
-  if (nq_full < nqt)  // the ragged last row of query tiles, all splits
-    hipLaunchKernelGGL((score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, true>), dim3(nsplit, 1),
-                       dim3(kPfWaves * 64), 0, st, a, nq_full, 0);
-  if (ns_full < nsplit && nq_full > 0)  // the ragged last split, whole query tiles
-    hipLaunchKernelGGL((score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, true>), dim3(1, nq_full),
-                       dim3(kPfWaves * 64), 0, st, a, 0, ns_full);
+  const bool l0 = nq_full > 0 && ns_full > 0, l1 = nq_full < nqt, l2 = ns_full < nsplit && nq_full > 0;
+  // the start event goes with the first launch issued, the stop event with the last
+  const int first = l0 ? 0 : l1 ? 1 : l2 ? 2 : -1, last = l2 ? 2 : l1 ? 1 : l0 ? 0 : -1;
+  auto e0 = [&](int i) { return i == first ? ev0 : nullptr; };
+  auto e1 = [&](int i) { return i == last ? ev1 : nullptr; };
+  if (l0)
+    hipExtLaunchKernelGGL((score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, false>), dim3(ns_full, nq_full),
+                          dim3(kPfWaves * 64), 0, st, e0(0), e1(0), 0, a, 0, 0);
+  if (l1)  // the ragged last row of query tiles, all splits
+    hipExtLaunchKernelGGL((score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, true>), dim3(nsplit, 1),
+                          dim3(kPfWaves * 64), 0, st, e0(1), e1(1), 0, a, nq_full, 0);
+  if (l2)  // the ragged last split, whole query tiles
+    hipExtLaunchKernelGGL((score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, true>), dim3(1, nq_full),
+                          dim3(kPfWaves * 64), 0, st, e0(2), e1(2), 0, a, 0, ns_full);
+  if (first < 0) {  // nothing to launch: the events mark the empty interval
+    if (ev0 && hipEventRecord(ev0, st) != hipSuccess) return hipErrorInvalidValue;
+    if (ev1 && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -333,12 +344,12 @@ bool prefill_supported(int h, int ld, int Lmax) {
          (uint64_t)Lmax * 256 <= 0x7FFFFFFFull;
 }
 
-hipError_t launch_score_prefill(const PrefillArgs &a, hipStream_t st) {
-  if (a.h <= 1) return launch_hp<1>(a, st);
-  if (a.h <= 2) return launch_hp<2>(a, st);
-  if (a.h <= 4) return launch_hp<4>(a, st);
-  if (a.h <= 8) return launch_hp<8>(a, st);
-  if (a.h <= 16) return launch_hp<16>(a, st);
+hipError_t launch_score_prefill(const PrefillArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  if (a.h <= 1) return launch_hp<1>(a, st, ev0, ev1);
+  if (a.h <= 2) return launch_hp<2>(a, st, ev0, ev1);
+  if (a.h <= 4) return launch_hp<4>(a, st, ev0, ev1);
+  if (a.h <= 8) return launch_hp<8>(a, st, ev0, ev1);
+  if (a.h <= 16) return launch_hp<16>(a, st, ev0, ev1);
   return hipErrorInvalidValue;
 }
 

@@ -23,6 +23,8 @@
 // stores spread through the key stream cost more HBM time than their bytes.
 // The epilogue also builds a 4096-bin histogram of the top 12 bits of each
 // score's order key, the first radix digit of the per-row top-k.
+#include <hip/hip_ext.h>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -207,26 +209,30 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
 }
 
 template <int HT, bool GATHER>
-static hipError_t launch_ht(const ScoreArgs &a, hipStream_t st) {
+static hipError_t launch_ht(const ScoreArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   dim3 grid((a.ncols + a.chunk - 1) / a.chunk, a.T);
   // two 16-key tiles per wave step: fewer registers, more waves per CU
   constexpr int U = 2;
   if (a.chunk > kMaxScoreChunk) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((score_rows_kernel<HT, GATHER, U>), grid, dim3(256), 0, st, a);
+  hipExtLaunchKernelGGL((score_rows_kernel<HT, GATHER, U>), grid, dim3(256), 0, st, ev0, ev1, 0, a);
   return hipGetLastError();
 }
 
 template <bool GATHER>
-static hipError_t launch_g(const ScoreArgs &a, hipStream_t st) {
-  if (a.nh <= 16) return launch_ht<1, GATHER>(a, st);
-  if (a.nh <= 32) return launch_ht<2, GATHER>(a, st);
-  if (a.nh <= 64) return launch_ht<4, GATHER>(a, st);
-  return launch_ht<8, GATHER>(a, st);
+static hipError_t launch_g(const ScoreArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  if (a.nh <= 16) return launch_ht<1, GATHER>(a, st, ev0, ev1);
+  if (a.nh <= 32) return launch_ht<2, GATHER>(a, st, ev0, ev1);
+  if (a.nh <= 64) return launch_ht<4, GATHER>(a, st, ev0, ev1);
+  return launch_ht<8, GATHER>(a, st, ev0, ev1);
 }
 
-hipError_t launch_score_rows(const ScoreArgs &a, hipStream_t st) {
-  if (a.T <= 0 || a.ncols <= 0) return hipSuccess;
-  return a.cand ? launch_g<true>(a, st) : launch_g<false>(a, st);
+hipError_t launch_score_rows(const ScoreArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  if (a.T <= 0 || a.ncols <= 0) {  // nothing to launch: the events mark the empty interval
+    if (ev0 && hipEventRecord(ev0, st) != hipSuccess) return hipErrorInvalidValue;
+    if (ev1 && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;
+    return hipSuccess;
+  }
+  return a.cand ? launch_g<true>(a, st, ev0, ev1) : launch_g<false>(a, st, ev0, ev1);
 }
 
 }  // namespace misa
