@@ -52,6 +52,7 @@ CASES = [
     (2, 4133, 6, 8, 2),
     (2, 2500, 9, 20, 3),
     (1, 17, 3, 64, 4),
+    (2, 1500, 4, 128, 5),  # the largest head count the kernels take (MISA_MAX_HEADS)
 ]
 
 
