@@ -25,6 +25,12 @@
 
 namespace misa {
 
+// A 16-byte value with every word ANDed with m (0 or all ones): masks a value
+// loaded from a clamped address, with no branch around the load.
+static __device__ __forceinline__ uint4 mask_u4(uint4 v, uint32_t m) {
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
 template <int HT>
 __global__ __launch_bounds__(256) void hisa_block_kernel(HisaArgs a) {
   __shared__ float red[4][kD];
@@ -78,11 +84,16 @@ __global__ __launch_bounds__(256) void hisa_block_kernel(HisaArgs a) {
     for (int m0 = 0; m0 < a.nh; m0 += 64) {
       const int m = m0 + (tid >> 2);
       float x = 0.f;
-      if (m < a.nh) {
-        const uint16_t *qv = a.q + ((size_t)t * a.H + head_of(m)) * kD + qq * 32;
+      // loads from a clamped head, rows past nh masked (no branch around them)
+      const uint32_t mm = m < a.nh ? 0xFFFFFFFFu : 0u;
+      const uint16_t *qv = a.q + ((size_t)t * a.H + head_of(min(m, a.nh - 1))) * kD + qq * 32;
+      uint4 qx[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) qx[u] = mask_u4(*(const uint4 *)(qv + u * 8), mm);
+      {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const uint4 v = *(const uint4 *)(qv + u * 8);
+          const uint4 v = qx[u];
           const uint32_t y[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -113,21 +124,30 @@ __global__ __launch_bounds__(256) void hisa_block_kernel(HisaArgs a) {
       if (bb > bt) srow[bb] = -INFINITY;
     return;
   }
+  // Head rows (A operand) and the weights of this lane's rows: two batched
+  // rounds of loads (head ids, then rows and weights) from clamped indices,
+  // rows past nh masked, so that no load waits behind a branch
   bf16x8 qa[HT][4];
   float wv[HT][4];
+  {
+    int jq[HT], jw[HT][4];
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const int m = ht * 16 + col;
+    for (int ht = 0; ht < HT; ++ht) {
+      jq[ht] = head_of(min(ht * 16 + col, a.nh - 1));
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m < a.nh) v = *(const uint4 *)(a.q + ((size_t)t * a.H + head_of(m)) * kD + s * 32 + grp * 8);
-      qa[ht][s] = as_bf16x8(v);
+      for (int r = 0; r < 4; ++r) jw[ht][r] = head_of(min(ht * 16 + grp * 4 + r, a.nh - 1));
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int mr = ht * 16 + grp * 4 + r;
-      wv[ht][r] = mr < a.nh ? a.w[(size_t)t * a.H + head_of(mr)] : 0.f;
+    for (int ht = 0; ht < HT; ++ht) {
+      const uint32_t mq = ht * 16 + col < a.nh ? 0xFFFFFFFFu : 0u;
+      const uint16_t *qr = a.q + ((size_t)t * a.H + jq[ht]) * kD + grp * 8;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) qa[ht][s] = as_bf16x8(mask_u4(*(const uint4 *)(qr + s * 32), mq));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t wb = __float_as_uint(a.w[(size_t)t * a.H + jw[ht][r]]);
+        wv[ht][r] = __uint_as_float(wb & (ht * 16 + grp * 4 + r < a.nh ? 0xFFFFFFFFu : 0u));
+      }
     }
   }
   const bool ok = b < bt;

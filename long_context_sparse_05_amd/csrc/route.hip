@@ -23,6 +23,12 @@
 
 namespace misa {
 
+// A 16-byte value with every word ANDed with m (0 or all ones): masks a value
+// loaded from a clamped address, with no branch around the load.
+static __device__ __forceinline__ uint4 mask_u4(uint4 v, uint32_t m) {
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
 template <int HT>
 __global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a) {
   __shared__ float part[4][HT * 16];
@@ -45,14 +51,16 @@ __global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a) {
     // this thread's query slices for the head dots below, requested first:
     // thread = (head j = tid/4 + 64*round, 32-dim quarter qq)
     const int qq = tid & 3;
+    // (loads from clamped indices, masked afterwards: a load under a branch
+    // would make each wait for every load before it)
     uint4 qv[2][4];
 #pragma unroll
     for (int rd = 0; rd < 2; ++rd) {
       const int j = rd * 64 + (tid >> 2);
+      const uint32_t mj = j < a.H ? 0xFFFFFFFFu : 0u;
+      const uint4 *qr = (const uint4 *)(a.q + ((size_t)t * a.H + min(j, a.H - 1)) * kD + qq * 32);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        qv[rd][u] = j < a.H ? ((const uint4 *)(a.q + ((size_t)t * a.H + j) * kD + qq * 32))[u]
-                            : make_uint4(0, 0, 0, 0);
+      for (int u = 0; u < 4; ++u) qv[rd][u] = mask_u4(qr[u], mj);
     }
     const uint16_t *kb = a.keys + (size_t)sq * a.Lmax * kD + dc * 8;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -61,7 +69,7 @@ __global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int i = i0 + 16 * u;
-        v[u] = i <= p ? *(const uint4 *)(kb + (size_t)i * kD) : make_uint4(0, 0, 0, 0);
+        v[u] = mask_u4(*(const uint4 *)(kb + (size_t)min(i, p) * kD), i <= p ? 0xFFFFFFFFu : 0u);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -117,31 +125,36 @@ __global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a) {
     return;
   }
 
+  // every load issued at once, from clamped indices, and masked afterwards
+  // (a load under a branch would make each step wait for all before it)
   bf16x8 qa[HT][4];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
     const int m = ht * 16 + col;
+    const uint32_t mq = m < a.H ? 0xFFFFFFFFu : 0u;
+    const uint16_t *qr = a.q + ((size_t)t * a.H + min(m, a.H - 1)) * kD + grp * 8;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m < a.H) v = *(const uint4 *)(a.q + ((size_t)t * a.H + m) * kD + s * 32 + grp * 8);
-      qa[ht][s] = as_bf16x8(v);
-    }
+    for (int s = 0; s < 4; ++s) qa[ht][s] = as_bf16x8(mask_u4(*(const uint4 *)(qr + s * 32), mq));
   }
   const int b = b0 + wave * 16 + col;
   const bool ok = b < bt;
+  const uint32_t mb = ok ? 0xFFFFFFFFu : 0u;
   const float *pb = a.pooled + ((size_t)sq * a.Mmax + (ok ? b : 0)) * kD + grp * 8;
+  uint4 xr[4][2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    xr[s][0] = mask_u4(*(const uint4 *)(pb + s * 32), mb);
+    xr[s][1] = mask_u4(*(const uint4 *)(pb + s * 32 + 4), mb);
+  }
   f32x4 acc[HT];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) acc[ht] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    float4 x0 = make_float4(0.f, 0.f, 0.f, 0.f), x1 = x0;
-    if (ok) {
-      x0 = *(const float4 *)(pb + s * 32);
-      x1 = *(const float4 *)(pb + s * 32 + 4);
-    }
-    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    const uint4 x0 = xr[s][0], x1 = xr[s][1];
+    const float xs[8] = {__uint_as_float(x0.x), __uint_as_float(x0.y), __uint_as_float(x0.z),
+                         __uint_as_float(x0.w), __uint_as_float(x1.x), __uint_as_float(x1.y),
+                         __uint_as_float(x1.z), __uint_as_float(x1.w)};
     u16x8 hi, mi, lo;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -193,27 +206,31 @@ __global__ __launch_bounds__(256) void route_final_kernel(RouteArgs a) {
     for (int i = tid; i < kHistBins / 4; i += 256) zh[i] = make_uint4(0, 0, 0, 0);
     if (tid < 8) a.zero_ctr[(size_t)t * 8 + tid] = 0u;
   }
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  // this thread's head weight (clamped index, used for tid < H), requested
+  // with the partials: batches of eight in flight, from clamped indices, the
+  // ones past the quarter masked to +0 (no branch around a load), added in
+  // order; the second 64 heads only when H > 64
+  const float wpre = a.w[(size_t)t * a.H + min(tid, a.H - 1)];
+  for (int u = 0; u < 2 && 64 * u < a.H; ++u) {
     const int j = lane + 64 * u;
-    if (j < a.H) {
-      float s = 0.f;
-      int c = c0;
-      for (; c + 8 <= c1; c += 8) {
-        float v[8];
+    const float *pj = pp + min(j, a.H - 1);
+    float s = 0.f;
+    for (int c = c0; c < c1; c += 8) {
+      float v[8];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) v[x] = pp[(size_t)(c + x) * a.H + j];
-#pragma unroll
-        for (int x = 0; x < 8; ++x) s += v[x];
+      for (int x = 0; x < 8; ++x) {
+        const uint32_t m = c + x < c1 ? 0xFFFFFFFFu : 0u;
+        v[x] = __uint_as_float(__float_as_uint(pj[(size_t)min(c + x, c1 - 1) * a.H]) & m);
       }
-      for (; c < c1; ++c) s += pp[(size_t)c * a.H + j];
-      red[quarter][j] = s;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) s += v[x];
     }
+    if (j < a.H) red[quarter][j] = s;
   }
   __syncthreads();
   if (tid < a.H) {
     const float s = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
-    float wj = a.w[(size_t)t * a.H + tid];
+    float wj = wpre;
     if (a.mode == 1) wj = fabsf(wj);
     gs[tid] = wj * s;
     if (a.g) a.g[(size_t)t * a.H + tid] = gs[tid];
