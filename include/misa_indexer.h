@@ -29,6 +29,11 @@
  *   - Tensor pointers are DEVICE pointers (hipMalloc'd or from a framework
  *     allocator).  The caller owns every buffer; the library keeps no pointer
  *     after returning, allocates nothing and holds no global state.
+ *   - keys, q, pooled keys, workspaces and misa_score's output are moved in
+ *     16-byte vectors: their base addresses must be 16-byte aligned (any
+ *     allocator's are; a view into one may not be), else the call returns
+ *     MISA_ERR_UNSUPPORTED.  Every other pointer needs only its element's
+ *     natural alignment (misa_topk's score rows included).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call only enqueues kernels on it: no host synchronisation, no
  *     allocation, no memset node (graph capture is safe).

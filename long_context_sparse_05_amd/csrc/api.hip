@@ -21,11 +21,16 @@ constexpr int kMaxRows = 65535;  // rows go on grid dimension y
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
+// Keys, queries, pooled keys, workspaces and misa_score's output are moved in
+// 16-byte vectors: their base addresses must be 16-byte aligned.
+bool a16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
 int check_batch(const misa_batch *b, bool need_q) {
   if (!b) return MISA_ERR_NULL;
   if (!b->keys) return MISA_ERR_NULL;
   if (need_q && (!b->q || !b->w || !b->q_seq || !b->q_pos)) return MISA_ERR_NULL;
   if (b->d != MISA_D) return MISA_ERR_UNSUPPORTED;
+  if (!a16(b->keys) || (need_q && !a16(b->q))) return MISA_ERR_UNSUPPORTED;
   if (b->S < 1 || b->Lmax < 1) return MISA_ERR_SHAPE;
   if (need_q) {
     if (b->T < 1 || b->H < 1) return MISA_ERR_SHAPE;
@@ -299,6 +304,7 @@ int misa_pool(const misa_batch *b, int32_t B, float *pooled, void *stream) {
   int rc = check_batch(b, false);
   if (rc) return rc;
   if (!b->seq_lens || !pooled) return MISA_ERR_NULL;
+  if (!a16(pooled)) return MISA_ERR_UNSUPPORTED;
   if (B < 1 || B > b->Lmax) return MISA_ERR_SHAPE;
   if (b->S > kMaxRows) return MISA_ERR_UNSUPPORTED;
   return hip_status(launch_pool(b->keys, b->seq_lens, b->S, b->Lmax, B, pooled,
@@ -310,6 +316,7 @@ int misa_pool_append(const misa_batch *b, int32_t B, const int32_t *old_lens, in
   int rc = check_batch(b, false);
   if (rc) return rc;
   if (!b->seq_lens || !old_lens || !pooled) return MISA_ERR_NULL;
+  if (!a16(pooled)) return MISA_ERR_UNSUPPORTED;
   if (B < 1 || B > b->Lmax || max_new < 0 || max_new > b->Lmax) return MISA_ERR_SHAPE;
   if (b->S > kMaxRows) return MISA_ERR_UNSUPPORTED;
   return hip_status(launch_pool_append(b->keys, b->seq_lens, old_lens, max_new, b->S, b->Lmax, B,
@@ -358,6 +365,7 @@ int misa_route(const misa_batch *b, const float *pooled, int32_t B, int32_t h, i
   int rc = check_batch(b, true);
   if (rc) return rc;
   if (!pooled || !heads || !ws) return MISA_ERR_NULL;
+  if (!a16(pooled) || !a16(ws)) return MISA_ERR_UNSUPPORTED;
   if (B < 1 || B > b->Lmax || h < 1 || h > b->H) return MISA_ERR_SHAPE;
   if (mode != 0 && mode != 1) return MISA_ERR_SHAPE;
   if (ws_bytes < route_bytes(b, B)) return MISA_ERR_WORKSPACE;
@@ -371,6 +379,7 @@ int misa_score(const misa_batch *b, const int32_t *heads, int32_t h, float *scor
   int rc = check_batch(b, true);
   if (rc) return rc;
   if (!scores) return MISA_ERR_NULL;
+  if (!a16(scores)) return MISA_ERR_UNSUPPORTED;
   if (heads && (h < 1 || h > b->H)) return MISA_ERR_SHAPE;
   if (use_prefill(b, heads, h))
     return hip_status(launch_score_prefill(make_prefill_args(b, heads, h, scores),
@@ -388,6 +397,7 @@ int misa_score(const misa_batch *b, const int32_t *heads, int32_t h, float *scor
 int misa_topk(const float *scores, int32_t rows, int32_t ld, const int32_t *row_len, int32_t k,
               int32_t *idx, float *val, void *ws, size_t ws_bytes, void *stream) {
   if (!scores || !row_len || !idx || !ws) return MISA_ERR_NULL;
+  if (!a16(ws)) return MISA_ERR_UNSUPPORTED;
   if (rows < 1 || ld < 1 || k < 1) return MISA_ERR_SHAPE;
   if (rows > kMaxRows) return MISA_ERR_UNSUPPORTED;
   const SelectLayout L = select_layout(rows, ld, k, false);
@@ -402,6 +412,7 @@ int misa_score_topk_ev(const misa_batch *b, const int32_t *heads, int32_t h, int
   int rc = check_batch(b, true);
   if (rc) return rc;
   if (!idx || !ws) return MISA_ERR_NULL;
+  if (!a16(ws)) return MISA_ERR_UNSUPPORTED;
   if (heads && (h < 1 || h > b->H)) return MISA_ERR_SHAPE;
   if (k < 1 || k > b->Lmax) return MISA_ERR_SHAPE;
   const SelectLayout L = select_layout(b->T, b->Lmax, k, true);
@@ -440,6 +451,7 @@ int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t
   int rc = check_batch(b, true);
   if (rc) return rc;
   if (!pooled || !heads || !idx || !ws) return MISA_ERR_NULL;
+  if (!a16(pooled) || !a16(ws)) return MISA_ERR_UNSUPPORTED;
   if (B < 1 || B > b->Lmax || h < 1 || h > b->H) return MISA_ERR_SHAPE;
   if (mode != 0 && mode != 1) return MISA_ERR_SHAPE;
   if (k < 1 || k > b->Lmax) return MISA_ERR_SHAPE;
@@ -482,6 +494,7 @@ int misa_rerank(const misa_batch *b, const int32_t *cand, int32_t kc, int32_t k,
   int rc = check_batch(b, true);
   if (rc) return rc;
   if (!cand || !idx || !ws) return MISA_ERR_NULL;
+  if (!a16(ws)) return MISA_ERR_UNSUPPORTED;
   if (k < 1 || kc < k || kc > b->Lmax) return MISA_ERR_SHAPE;
   const SelectLayout L = select_layout(b->T, kc, k, true);
   if (ws_bytes < L.total) return MISA_ERR_WORKSPACE;
@@ -523,6 +536,7 @@ static int hisa_check(const misa_batch *b, const float *pooled, int B, int m, co
   int rc = check_batch(b, true);
   if (rc) return rc;
   if (!pooled) return MISA_ERR_NULL;
+  if (!a16(pooled)) return MISA_ERR_UNSUPPORTED;
   if (B < 1 || B > b->Lmax) return MISA_ERR_SHAPE;
   const int Mmax = (b->Lmax + B - 1) / B;
   if (m < 1 || m > Mmax || k < 1 || k > b->Lmax) return MISA_ERR_SHAPE;
@@ -546,6 +560,7 @@ int hisa_blocks(const misa_batch *b, const float *pooled, int32_t B, int32_t m,
   int rc = hisa_check(b, pooled, B, m, heads, h, 1);
   if (rc) return rc;
   if (!ws) return MISA_ERR_NULL;
+  if (!a16(ws)) return MISA_ERR_UNSUPPORTED;
   const HisaLayout HL = hisa_layout(b, B, m, 1);
   if (ws_bytes < HL.total) return MISA_ERR_WORKSPACE;
   const hipStream_t st = (hipStream_t)stream;
@@ -559,6 +574,7 @@ int hisa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t
   int rc = hisa_check(b, pooled, B, m, heads, h, k);
   if (rc) return rc;
   if (!idx || !ws) return MISA_ERR_NULL;
+  if (!a16(ws)) return MISA_ERR_UNSUPPORTED;
   const HisaLayout HL = hisa_layout(b, B, m, k);
   if (ws_bytes < HL.total) return MISA_ERR_WORKSPACE;
   const hipStream_t st = (hipStream_t)stream;

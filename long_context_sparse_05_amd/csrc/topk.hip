@@ -153,8 +153,13 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a) {
         sh[8] = run_sel;
         sh[9] = run_cnd;
       } else {
-        sh[8] = (total >> 16) ? atomicAdd(&cnt[0], total >> 16) : 0u;
-        sh[9] = (total & 0xFFFFu) ? atomicAdd(&cnt[1], total & 0xFFFFu) : 0u;
+        // counters 0 and 1 as one 64-bit word (low: selected, high:
+        // candidates; a row's counts stay far below 2^32, so no carry
+        // crosses): one atomic, one round trip
+        const unsigned long long o = atomicAdd(
+            (unsigned long long *)cnt, ((unsigned long long)(total & 0xFFFFu) << 32) | (total >> 16));
+        sh[8] = (uint32_t)o;
+        sh[9] = (uint32_t)(o >> 32);
       }
     }
     run_sel += total >> 16;
@@ -297,10 +302,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_finish_kernel(TopkArgs a) {
   const int tid = threadIdx.x;
   const uint32_t *cnt = a.counters + (size_t)r * kRowCounters;
   Thresh th;
-  th.b1 = (int)cnt[4];
-  th.above = cnt[5];
-  th.eq = cnt[6];
-  th.kk = cnt[7];
+  {
+    const uint4 c4 = *(const uint4 *)(cnt + 4);  // the filter's b1, above, eq, kk in one load
+    th.b1 = (int)c4.x;
+    th.above = c4.y;
+    th.eq = c4.z;
+    th.kk = c4.w;
+  }
 
   int32_t *irow = a.idx + (size_t)r * a.k;
   float *vrow = a.val ? a.val + (size_t)r * a.k : nullptr;
@@ -315,11 +323,17 @@ __global__ __launch_bounds__(kSelThreads) void topk_finish_kernel(TopkArgs a) {
   const int32_t *mrow = MAP ? a.map + (size_t)r * a.ld : nullptr;
   const bool keep = th.eq <= (uint32_t)a.cap;
   const int ncur = keep ? (int)min(th.eq, (uint32_t)a.cap) : 0;
-  if (keep) {
+  if (keep) {  // four candidates per thread in flight (clamped loads, guarded stores)
     const uint2 *crow = a.cand + (size_t)r * a.cap;
-    for (int i = tid; i < ncur; i += NT) {
-      const uint2 e = crow[i];
-      cs[i] = composite(e.x, MAP ? mrow[e.y] : (int)e.y);
+    for (int i0 = 0; i0 < ncur; i0 += 4 * NT) {
+      uint2 e[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) e[u] = crow[min(i0 + u * NT + tid, ncur - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * NT + tid;
+        if (i < ncur) cs[i] = composite(e[u].x, MAP ? mrow[e[u].y] : (int)e[u].y);
+      }
     }
   }
   if (tid == 0) ctr[0] = th.above;

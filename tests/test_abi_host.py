@@ -147,3 +147,20 @@ def test_validation_before_any_hip_call(lib):
     assert lib.hisa_indexer(ctypes.byref(b), F, 64, 4, None, 0, 8, F, None, F, small, None) == ERR_WORKSPACE
     assert lib.hisa_blocks(ctypes.byref(b), F, 64, 4, None, 0, F, F, F, small, None) == ERR_WORKSPACE
     assert lib.hisa_blocks(ctypes.byref(b), F, 64, 4, None, 0, F, F, None, big, None) == ERR_NULL
+    # base addresses moved in 16-byte vectors must be 16-byte aligned
+    U = P(FAKE + 4)
+    assert lib.misa_pool(ctypes.byref(batch(keys=FAKE + 4)), 64, F, None) == ERR_UNSUPPORTED
+    assert lib.misa_pool(ctypes.byref(b), 64, U, None) == ERR_UNSUPPORTED
+    assert lib.misa_pool_append(ctypes.byref(b), 64, F, 1, U, None) == ERR_UNSUPPORTED
+    assert lib.misa_route(ctypes.byref(batch(q=FAKE + 8)), F, 64, 8, 0, F, None, F, big, None) == ERR_UNSUPPORTED
+    assert lib.misa_route(ctypes.byref(b), U, 64, 8, 0, F, None, F, big, None) == ERR_UNSUPPORTED
+    assert lib.misa_route(ctypes.byref(b), F, 64, 8, 0, F, None, U, big, None) == ERR_UNSUPPORTED
+    assert lib.misa_score(ctypes.byref(b), None, 0, U, None) == ERR_UNSUPPORTED
+    assert lib.misa_score_topk(ctypes.byref(b), F, 8, 64, F, None, U, big, None) == ERR_UNSUPPORTED
+    assert lib.misa_indexer(ctypes.byref(b), F, 64, 8, 0, 64, F, None, F, None, U, big, None) == ERR_UNSUPPORTED
+    assert lib.misa_rerank(ctypes.byref(b), F, 128, 64, F, None, U, big, None) == ERR_UNSUPPORTED
+    assert lib.misa_topk(F, 4, 64, F, 8, F, None, U, big, None) == ERR_UNSUPPORTED
+    assert lib.hisa_indexer(ctypes.byref(b), U, 64, 4, None, 0, 8, F, None, F, big, None) == ERR_UNSUPPORTED
+    assert lib.hisa_blocks(ctypes.byref(b), F, 64, 4, None, 0, F, F, U, big, None) == ERR_UNSUPPORTED
+    # score rows given to misa_topk may start anywhere a float may
+    assert lib.misa_topk(U, 4, 64, F, 8, F, None, F, small, None) == ERR_WORKSPACE
