@@ -130,14 +130,22 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a) {
   uint32_t run_sel = 0, run_cnd = 0;
   for (int sb = c0; sb < c1; sb += kSub) {  // uniform trip count
     if (sb != c0) load_round(sb, sv);
+    // the round's map entries, all issued at once from clamped columns (a
+    // load under a branch would wait for every load before it)
+    int32_t mv[4][4];
+    if constexpr (MAP) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mv[u][e] = mrow[min(sb + u * 1024 + 4 * tid + e, c1 - 1)];
+    }
     uint32_t fs = 0, fc = 0;  // this thread's 16 columns: above b1 / equal to b1
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int c = sb + u * 1024 + 4 * tid + e;
-        bool valid = c < c1;
-        if (MAP && valid) valid = mrow[c] >= 0;
+        const bool valid = c < c1 && (!MAP || mv[u][e] >= 0);
         const int dg = (int)(order_key(sv[u][e]) >> kHistShift);
         fs |= (valid && dg > th.b1 ? 1u : 0u) << (u * 4 + e);
         fc |= (valid && keep && dg == th.b1 ? 1u : 0u) << (u * 4 + e);
@@ -174,7 +182,7 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a) {
         const int c = sb + u * 1024 + 4 * tid + e;
         if ((fs >> bit) & 1u) {
           if (so < th.above) {
-            irow[so] = MAP ? mrow[c] : c;
+            irow[so] = MAP ? mv[u][e] : c;
             if (vrow) vrow[so] = sv[u][e];
           }
           ++so;
@@ -329,10 +337,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_finish_kernel(TopkArgs a) {
       uint2 e[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) e[u] = crow[min(i0 + u * NT + tid, ncur - 1)];
+      int32_t tok[4];  // every clamped entry holds a valid column
+#pragma unroll
+      for (int u = 0; u < 4; ++u) tok[u] = MAP ? mrow[e[u].y] : (int)e[u].y;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = i0 + u * NT + tid;
-        if (i < ncur) cs[i] = composite(e[u].x, MAP ? mrow[e[u].y] : (int)e[u].y);
+        if (i < ncur) cs[i] = composite(e[u].x, tok[u]);
       }
     }
   }
@@ -589,15 +600,27 @@ __device__ __forceinline__ void rowselect_row(const TopkArgs &a, const int r) {
       }
     }
   };
-  auto valid_col = [&](int c) { return c < n && (!MAP || mrow[c] >= 0); };
-  auto hist_round = [&](int base, const float (&sv)[U][4]) {
-    const bool all = !MAP && base + kSelRound <= n;  // uniform: no per-column test
+  // a round's map entries (token ids, -1 = empty slot), all loads issued at
+  // once from columns clamped into the row: a load under a branch would wait
+  // for every load before it
+  auto load_map = [&](int base, int32_t (&mv)[U][4]) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (all || valid_col(base + u * NT * 4 + 4 * tid + e))
+      for (int e = 0; e < 4; ++e) mv[u][e] = mrow[min(base + u * NT * 4 + 4 * tid + e, n - 1)];
+  };
+  auto hist_round = [&](int base, const float (&sv)[U][4]) {
+    const bool all = !MAP && base + kSelRound <= n;  // uniform: no per-column test
+    int32_t mv[U][4];
+    if constexpr (MAP) load_map(base, mv);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = base + u * NT * 4 + 4 * tid + e;
+        if (all || (c < n && (!MAP || mv[u][e] >= 0)))
           atomicAdd(&lh[order_key(sv[u][e]) >> kHistShift], 1u);
+      }
   };
 
   float sv[RR][U][4];
@@ -652,13 +675,15 @@ __device__ __forceinline__ void rowselect_row(const TopkArgs &a, const int r) {
   __syncthreads();
   // pass 2: emit the columns above b1, collect the columns equal to b1
   auto emit_round = [&](int base, const float (&sv)[U][4]) {
+    int32_t mv[U][4];
+    if constexpr (MAP) load_map(base, mv);
     uint32_t fs = 0, fc = 0;  // this thread's 16 columns: above b1 / equal to b1
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int c = base + u * NT * 4 + 4 * tid + e;
-        const bool valid = valid_col(c);
+        const bool valid = c < n && (!MAP || mv[u][e] >= 0);
         const int dg = (int)(order_key(sv[u][e]) >> kHistShift);
         fs |= (valid && dg > th.b1 ? 1u : 0u) << (u * 4 + e);
         fc |= (valid && keep && dg == th.b1 ? 1u : 0u) << (u * 4 + e);
@@ -685,13 +710,13 @@ __device__ __forceinline__ void rowselect_row(const TopkArgs &a, const int r) {
         const int c = base + u * NT * 4 + 4 * tid + e;
         if ((fs >> bit) & 1u) {
           if (so < th.above) {
-            irow[so] = MAP ? mrow[c] : c;
+            irow[so] = MAP ? mv[u][e] : c;
             if (vrow) vrow[so] = sv[u][e];
           }
           ++so;
         }
         if ((fc >> bit) & 1u) {
-          if (co < (uint32_t)kSelCap) cs[co] = composite(order_key(sv[u][e]), MAP ? mrow[c] : c);
+          if (co < (uint32_t)kSelCap) cs[co] = composite(order_key(sv[u][e]), MAP ? mv[u][e] : c);
           ++co;
         }
       }
