@@ -65,11 +65,11 @@ extern "C" {
 #define MISA_OK 0
 #define MISA_ERR_NULL (-1)        /* a required pointer is NULL                 */
 #define MISA_ERR_SHAPE (-2)       /* a size or count is out of range            */
-#define MISA_ERR_UNSUPPORTED (-3) /* a valid request this build does not handle */
+#define MISA_ERR_UNSUPPORTED (-3) /* a valid request the library does not handle */
 #define MISA_ERR_WORKSPACE (-4)   /* workspace smaller than required            */
 #define MISA_ERR_HIP (-5)         /* a HIP launch or runtime call failed        */
 
-/* The key dimension this build supports. */
+/* The key dimension the library supports. */
 #define MISA_D 128
 /* Largest number of indexer heads H (and routed heads h). */
 #define MISA_MAX_HEADS 128

@@ -255,7 +255,7 @@ const char *misa_status_str(int status) {
     case MISA_OK: return "ok";
     case MISA_ERR_NULL: return "a required pointer is NULL";
     case MISA_ERR_SHAPE: return "a size or count is out of range";
-    case MISA_ERR_UNSUPPORTED: return "unsupported argument for this build";
+    case MISA_ERR_UNSUPPORTED: return "unsupported argument (the library does not handle it)";
     case MISA_ERR_WORKSPACE: return "workspace is smaller than required";
     case MISA_ERR_HIP: return "a HIP launch or runtime call failed";
     default: return "unknown status";
