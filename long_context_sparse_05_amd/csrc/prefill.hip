@@ -318,15 +318,18 @@ static hipError_t launch_hp(const PrefillArgs &a, hipStream_t st, hipEvent_t ev0
   const int first = l0 ? 0 : l1 ? 1 : l2 ? 2 : -1, last = l2 ? 2 : l1 ? 1 : l0 ? 0 : -1;
   auto e0 = [&](int i) { return i == first ? ev0 : nullptr; };
   auto e1 = [&](int i) { return i == last ? ev1 : nullptr; };
-  if (l0)
-    hipExtLaunchKernelGGL((score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, false>), dim3(ns_full, nq_full),
-                          dim3(kPfWaves * 64), 0, st, e0(0), e1(0), 0, a, 0, 0);
+  // plain launches unless the measurement hook asks for events
+  auto launch = [&](int i, auto kernel, dim3 grid, int qtile0, int split0) {
+    if (e0(i) || e1(i))
+      hipExtLaunchKernelGGL(kernel, grid, dim3(kPfWaves * 64), 0, st, e0(i), e1(i), 0, a, qtile0, split0);
+    else
+      hipLaunchKernelGGL(kernel, grid, dim3(kPfWaves * 64), 0, st, a, qtile0, split0);
+  };
+  if (l0) launch(0, score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, false>, dim3(ns_full, nq_full), 0, 0);
   if (l1)  // the ragged last row of query tiles, all splits
-    hipExtLaunchKernelGGL((score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, true>), dim3(nsplit, 1),
-                          dim3(kPfWaves * 64), 0, st, e0(1), e1(1), 0, a, nq_full, 0);
+    launch(1, score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, true>, dim3(nsplit, 1), nq_full, 0);
   if (l2)  // the ragged last split, whole query tiles
-    hipExtLaunchKernelGGL((score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, true>), dim3(1, nq_full),
-                          dim3(kPfWaves * 64), 0, st, e0(2), e1(2), 0, a, 0, ns_full);
+    launch(2, score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, true>, dim3(1, nq_full), 0, ns_full);
   if (first < 0) {  // nothing to launch: the events mark the empty interval
     if (ev0 && hipEventRecord(ev0, st) != hipSuccess) return hipErrorInvalidValue;
     if (ev1 && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;

@@ -214,7 +214,10 @@ static hipError_t launch_ht(const ScoreArgs &a, hipStream_t st, hipEvent_t ev0, 
   // two 16-key tiles per wave step: fewer registers, more waves per CU
   constexpr int U = 2;
   if (a.chunk > kMaxScoreChunk) return hipErrorInvalidValue;
-  hipExtLaunchKernelGGL((score_rows_kernel<HT, GATHER, U>), grid, dim3(256), 0, st, ev0, ev1, 0, a);
+  if (ev0 || ev1)  // the measurement hook: events stamped with the kernel's begin and end
+    hipExtLaunchKernelGGL((score_rows_kernel<HT, GATHER, U>), grid, dim3(256), 0, st, ev0, ev1, 0, a);
+  else
+    hipLaunchKernelGGL((score_rows_kernel<HT, GATHER, U>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
