@@ -191,9 +191,11 @@ def main(argv=None):
         return summarize_counters(args.workload, *args.summarize_counters)
     if args.copy_calibration:
         return copy_calibration()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the indexer path here is built and timed on a single "
-              "MI355X; --gpus %d is not supported" % args.gpus, file=sys.stderr)
+              "MI355X; %d GPUs (--gpus %d, WORLD_SIZE %d) is not supported"
+              % (max(args.gpus, world), args.gpus, world), file=sys.stderr)
         return 2
 
     import numpy as np
