@@ -582,13 +582,18 @@ int hisa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t
   int32_t *cand = (int32_t *)((char *)ws + HL.cand);
   rc = hisa_coarse(b, pooled, B, m, heads, h, ws, HL, kept, nullptr, st);
   if (rc) return rc;
-  if (launch_hisa_expand(kept, b->q_pos, b->T, m, B, cand, st) != hipSuccess) return MISA_ERR_HIP;
-  // token-level refinement: the indexer over the kept blocks' tokens
+  // token-level refinement: the indexer over the kept blocks' tokens (the
+  // scoring kernel expands the block ids and writes the token lists the
+  // select maps its columns through)
   const int kc = m * B;
   void *tws = (char *)ws + HL.tsel;
   ScoreArgs s = make_score_args(b, heads, heads ? h : b->H);
   s.scores = (float *)((char *)tws + HL.LT.scores);
-  s.cand = cand;
+  s.cand = nullptr;
+  s.kept = kept;
+  s.cand_out = cand;
+  s.nkept = m;
+  s.blk = B;
   s.ncols = kc;
   s.ld = kc;
   s.chunk = score_chunk(b->T, kc);

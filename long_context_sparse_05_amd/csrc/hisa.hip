@@ -19,7 +19,8 @@
 // holds and sums the four lane groups, giving one score per block column.
 // The extra workgroup per query scores the query's own last block, pooled
 // from the raw keys of [bt*B, p], and writes the query's block count.
-// hisa_expand_kernel turns the kept block ids into candidate token lists.
+// The refinement's scoring kernel expands the kept block ids into token
+// lists itself (score.hip, the kept-block gather).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -193,31 +194,12 @@ __global__ __launch_bounds__(256) void hisa_block_kernel(HisaArgs a) {
   }
 }
 
-__global__ void hisa_expand_kernel(const int32_t *kept, const int32_t *q_pos, int m, int B, int kc,
-                                   int32_t *cand) {
-  const int t = blockIdx.y;
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= kc) return;
-  const int i = c / B, o = c - i * B;
-  const int blk = kept[(size_t)t * m + i];
-  const int tok = blk * B + o;
-  cand[(size_t)t * kc + c] = (blk >= 0 && tok <= q_pos[t]) ? tok : -1;
-}
-
 hipError_t launch_hisa_blocks(const HisaArgs &a, hipStream_t st) {
   dim3 grid(a.nchunks + 1, a.T);
   if (a.nh <= 16) hipLaunchKernelGGL(hisa_block_kernel<1>, grid, dim3(256), 0, st, a);
   else if (a.nh <= 32) hipLaunchKernelGGL(hisa_block_kernel<2>, grid, dim3(256), 0, st, a);
   else if (a.nh <= 64) hipLaunchKernelGGL(hisa_block_kernel<4>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(hisa_block_kernel<8>, grid, dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_hisa_expand(const int32_t *kept, const int32_t *q_pos, int T, int m, int B,
-                              int32_t *cand, hipStream_t st) {
-  const int kc = m * B;
-  dim3 grid((kc + 255) / 256, T);
-  hipLaunchKernelGGL(hisa_expand_kernel, grid, dim3(256), 0, st, kept, q_pos, m, B, kc, cand);
   return hipGetLastError();
 }
 

@@ -16,6 +16,13 @@ struct ScoreArgs {
   const int32_t *q_pos;    // [T]
   const int32_t *heads;    // [T][nh] or nullptr (rows 0..nh-1 = heads 0..nh-1)
   const int32_t *cand;     // [T][ncols] token ids (-1 empty) or nullptr (column = token)
+  // With kept != nullptr the candidates are the tokens of kept blocks:
+  // column c is token kept[t][c / blk] * blk + c % blk (-1 for an empty block
+  // slot or past q_pos[t]); the kernel computes them and writes them to
+  // cand_out [T][ncols] for the select that follows.
+  const int32_t *kept;     // [T][nkept] block ids (-1 empty) or nullptr
+  int32_t *cand_out;
+  int nkept, blk;
   float *scores;           // [T][ld]
   uint32_t *hist;          // [T][4096] first-digit histogram (accumulated), or nullptr
   int nh, H, Lmax, T;
@@ -110,8 +117,6 @@ struct HisaArgs {
   int S, Lmax, T, H, nh, B, Mmax, nchunks;
 };
 hipError_t launch_hisa_blocks(const HisaArgs &a, hipStream_t st);
-hipError_t launch_hisa_expand(const int32_t *kept, const int32_t *q_pos, int T, int m, int B,
-                              int32_t *cand, hipStream_t st);
 hipError_t launch_route(const RouteArgs &a, hipStream_t st);
 // many queries of one sequence, H <= 64: one kernel, heads written directly
 hipError_t launch_route_tile(const RouteArgs &a, hipStream_t st);

@@ -94,9 +94,22 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
       }
     }
   }
-  const int32_t *crow = GATHER ? a.cand + (size_t)t * a.ncols : nullptr;
-  if (GATHER)
-    for (int c = c0 + threadIdx.x; c < c1; c += 256) ctok[c - c0] = crow[c];
+  if (GATHER) {
+    if (a.kept) {  // the tokens of the kept blocks, also written out for the select
+      const int32_t *krow = a.kept + (size_t)t * a.nkept;
+      int32_t *orow = a.cand_out + (size_t)t * a.ncols;
+      const int p = a.q_pos[t];
+      for (int c = c0 + threadIdx.x; c < c1; c += 256) {
+        const int i = c / a.blk, b = krow[i], tok = b * a.blk + (c - i * a.blk);
+        const int v = (b >= 0 && tok <= p) ? tok : -1;
+        ctok[c - c0] = v;
+        orow[c] = v;
+      }
+    } else {
+      const int32_t *crow = a.cand + (size_t)t * a.ncols;
+      for (int c = c0 + threadIdx.x; c < c1; c += 256) ctok[c - c0] = crow[c];
+    }
+  }
   if (hist || GATHER) __syncthreads();
 
   char *wt = (char *)tile[wave];
@@ -235,7 +248,7 @@ hipError_t launch_score_rows(const ScoreArgs &a, hipStream_t st, hipEvent_t ev0,
     if (ev1 && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;
     return hipSuccess;
   }
-  return a.cand ? launch_g<true>(a, st, ev0, ev1) : launch_g<false>(a, st, ev0, ev1);
+  return (a.cand || a.kept) ? launch_g<true>(a, st, ev0, ev1) : launch_g<false>(a, st, ev0, ev1);
 }
 
 }  // namespace misa
