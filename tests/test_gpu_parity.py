@@ -706,6 +706,38 @@ def test_indexer_fused_equals_separate_calls(S, Lmax, T, H, seed, mode):
                              parity.row_sbar(om["scores"][t], n))
 
 
+def test_indexer_many_decode_rows_take_the_streamed_select():
+    """Per-row decode scoring of 256 query rows over two sequences, prefixes
+    of 16384..20000 keys: the fused call scores the rows and selects them
+    with the streamed select (rows at or past 16384 columns); heads and
+    selections match the oracle for every row."""
+    abi = _abi()
+    S, Lmax, T, H = 2, 20000, 256, 16
+    rng = np.random.default_rng(77)
+    q_seq = np.repeat(np.arange(S, dtype=np.int32), T // S)
+    q_pos = rng.integers(16383, Lmax, size=T).astype(np.int32)
+    q_pos[:4] = [16383, 16384, Lmax - 1, 16390]
+    case = synth.random_case(S, Lmax, T, H, seed=13, q_pos=q_pos, q_seq=q_seq)
+    b = upload(case)
+    B, h, k = 128, 4, 300
+    pooled = abi.pool(b, B)
+    heads, idx, val = abi.indexer(b, pooled, B, h, k)
+    heads, idx, val = np_(heads), np_(idx), np_(val)
+    om = orc.misa(orc.Batch.from_case(case), B, h, k, want_scores=True)
+    checked = 0
+    for t in range(T):
+        if set(heads[t]) != set(om["heads"][t]):
+            assert parity.head_margin(om["g"][t], h) < 1e-4, t
+            continue
+        n = int(q_pos[t]) + 1
+        sb = parity.row_sbar(om["scores"][t], n)
+        parity.check_set(idx[t], om["idx"][t], lambda i: om["scores"][t, i], n, k, sb)
+        for i, v in zip(idx[t], val[t]):
+            assert abs(float(v) - om["scores"][t, i]) <= parity.REL * (abs(om["scores"][t, i]) + sb)
+        checked += 1
+    assert checked >= T - 4
+
+
 # ------------------------------------------------------- prefill tiling path
 PREFILL_CASES = [
     # Lmax, T, H, h, positions
