@@ -263,10 +263,10 @@ int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B,
 
 /*
  * hisa_indexer -- the hierarchical block-to-token indexer ("HISA: Efficient
- * Hierarchical Indexing for Fine-Grained Sparse Attention", abstract: a
- * block-level coarse filter scores pooled block representations and
- * discards irrelevant regions, then the original indexer runs only within
- * the retained candidate blocks; the token-level top-k output is kept).
+ * Hierarchical Indexing for Fine-Grained Sparse Attention", abstract: first
+ * whole blocks are ranked by a score on their pooled summaries and the
+ * low-ranked ones dropped, then the unchanged token-level indexer scores only
+ * the tokens of the blocks that survive and returns its usual top-k set).
  * Readings, the pages giving no formula: a block's representation is its
  * mean key (misa_pool's cache; the query's own last block is the mean over
  * [floor(p/B)*B, p]); its score is the indexer's form on that mean,

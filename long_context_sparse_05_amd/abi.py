@@ -61,6 +61,10 @@ def load():
         L.misa_rerank.argtypes = [BP, _P, _I, _I, _P, _P, _P, _SZ, _P]
         L.misa_indexer.argtypes = [BP, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]
         L.misa_indexer_ev.argtypes = [BP, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]
+        L.misa_pool_append.argtypes = [BP, _I, _P, _I, _P, _P]
+        L.hisa_indexer.argtypes = [BP, _P, _I, _I, _P, _I, _I, _P, _P, _P, _SZ, _P]
+        L.hisa_indexer_ev.argtypes = [BP, _P, _I, _I, _P, _I, _I, _P, _P, _P, _SZ, _P, _P, _P]
+        L.hisa_blocks.argtypes = [BP, _P, _I, _I, _P, _I, _P, _P, _P, _SZ, _P]
         for name in EXPORTS:
             getattr(L, name).restype = ctypes.c_int
         L.misa_status_str.argtypes = [ctypes.c_int]

@@ -1,9 +1,10 @@
 // hisa.hip -- the hierarchical indexer's coarse stage: block scores.
 //
 // "HISA: Efficient Hierarchical Indexing for Fine-Grained Sparse Attention"
-// (abstract): a block-level coarse filter scores pooled block
-// representations to discard irrelevant regions; a token-level refinement
-// then applies the original indexer only within the retained blocks.  Here
+// (abstract) searches in two passes: a cheap pass ranks whole blocks of the
+// prefix by a score computed on each block's pooled summary and drops the
+// low-ranked blocks, and the unchanged token-level indexer then looks only
+// at the tokens of the blocks that survive.  Here
 // a block's representation is its mean key (the pooled-key cache MISA's
 // router reads, "MISA: Mixture of Indexer Sparse Attention for Long-Context
 // LLM Inference", Technical Summary, Methodology: Lightweight Block-Pooled

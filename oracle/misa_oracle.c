@@ -432,11 +432,11 @@ int orc_misa_dagger(const uint16_t *keys, const uint16_t *q, const float *w,
 }
 
 /*
- * orc_hisa: the hierarchical block-to-token indexer ([HISA-AB]: a
- * block-level coarse filter scores pooled block representations to discard
- * irrelevant regions, then a token-level refinement applies the original
- * indexer only within the retained candidate blocks; the token-level top-k
- * pattern is kept).  Readings, the pages giving no formula:
+ * orc_hisa: the hierarchical block-to-token indexer ([HISA-AB], the
+ * abstract: a first pass ranks whole blocks by a score on each block's pooled
+ * summary and drops the low-ranked ones; the unchanged token-level indexer
+ * then scores only the tokens of the surviving blocks, and its per-query
+ * top-k token set stays the output).  Readings, the pages giving no formula:
  *   H1  a block's representation is the mean of its keys (R4's blocks, as
  *       MISA's router pools them); the query's own last block is the mean
  *       over its prefix tokens;

@@ -57,6 +57,8 @@ def lib():
         L.orc_rerank.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _I, _P, _P]
         L.orc_misa_dagger.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                       _I, _I, _P, _P, _P, _P]
+        L.orc_hisa.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _I,
+                               _P, _P, _P, _P]
         L.orc_num_threads.restype = _I
         L.orc_set_num_threads.argtypes = [_I]
         _lib = L
