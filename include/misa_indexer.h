@@ -28,7 +28,8 @@
  * Conventions for every call
  *   - Tensor pointers are DEVICE pointers (hipMalloc'd or from a framework
  *     allocator).  The caller owns every buffer; the library keeps no pointer
- *     after returning, allocates nothing and holds no global state.
+ *     after returning and allocates nothing.  Its one global object is the
+ *     static scratch array of misa_indexer_noalloc (see there).
  *   - keys, q, pooled keys, workspaces and misa_score's output are moved in
  *     16-byte vectors: their base addresses must be 16-byte aligned (any
  *     allocator's are; a view into one may not be), else the call returns
@@ -68,6 +69,8 @@ extern "C" {
 #define MISA_ERR_UNSUPPORTED (-3) /* a valid request the library does not handle */
 #define MISA_ERR_WORKSPACE (-4)   /* workspace smaller than required            */
 #define MISA_ERR_HIP (-5)         /* a HIP launch or runtime call failed        */
+#define MISA_ERR_TOO_LARGE (-6)   /* more scratch than misa_indexer_noalloc's
+                                     static buffer holds                        */
 
 /* The key dimension the library supports. */
 #define MISA_D 128
@@ -260,6 +263,31 @@ int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B,
                     float *head_score, int32_t *idx, float *val, void *ws,
                     size_t ws_bytes, void *stream, void *ev_start,
                     void *ev_stop);
+
+/*
+ * misa_indexer_noalloc -- misa_indexer for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, outputs
+ * and kernels as misa_indexer, without ws / ws_bytes: the scratch is a
+ * static device array of MISA_NOALLOC_SCRATCH_BYTES inside the library, one
+ * copy per GPU (on the device current at the call, which must be the
+ * stream's device), reserved when the library is loaded on that GPU and held
+ * until the process ends.  The first call on a device looks up that copy's
+ * address (hipGetSymbolAddress); no call allocates or frees memory.
+ *   Limit: a batch whose MISA_OP_INDEXER workspace (misa_workspace_bytes with
+ *   the same B, h, k) exceeds MISA_NOALLOC_SCRATCH_BYTES is rejected with
+ *   MISA_ERR_TOO_LARGE before anything is enqueued -- for example 16
+ *   sequences of 131072 keys need about 10.5 MiB, 64 such sequences do not
+ *   fit.
+ *   Every call on one GPU uses the same scratch, and a call leaves its
+ *   contents behind: calls on one GPU must be ordered (one stream, or events
+ *   between streams); calls that overlap race and give undefined results.
+ */
+#define MISA_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+int misa_indexer_noalloc(const misa_batch *b, const float *pooled, int32_t B,
+                         int32_t h, int32_t mode, int32_t k, int32_t *heads,
+                         float *head_score, int32_t *idx, float *val,
+                         void *stream);
 
 /*
  * hisa_indexer -- the hierarchical block-to-token indexer ("HISA: Efficient

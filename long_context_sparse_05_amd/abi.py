@@ -23,8 +23,12 @@ LIB_PATH = os.path.join(HERE, "libmisa_indexer.so")
 # Every entry point include/misa_indexer.h declares.
 EXPORTS = ("misa_workspace_bytes", "misa_pool", "misa_pool_append", "misa_route", "misa_score", "misa_topk",
            "misa_score_topk", "misa_score_topk_ev", "indexer_dense", "misa_rerank",
-           "misa_indexer", "misa_indexer_ev", "hisa_indexer", "hisa_indexer_ev", "hisa_blocks",
-           "misa_status_str")
+           "misa_indexer", "misa_indexer_ev", "misa_indexer_noalloc", "hisa_indexer",
+           "hisa_indexer_ev", "hisa_blocks", "misa_status_str")
+
+MISA_ERR_TOO_LARGE = -6
+# bytes of misa_indexer_noalloc's static scratch (MISA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 
 
 class MisaBatch(ctypes.Structure):
@@ -61,6 +65,7 @@ def load():
         L.misa_rerank.argtypes = [BP, _P, _I, _I, _P, _P, _P, _SZ, _P]
         L.misa_indexer.argtypes = [BP, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P]
         L.misa_indexer_ev.argtypes = [BP, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]
+        L.misa_indexer_noalloc.argtypes = [BP, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P]
         L.misa_pool_append.argtypes = [BP, _I, _P, _I, _P, _P]
         L.hisa_indexer.argtypes = [BP, _P, _I, _I, _P, _I, _I, _P, _P, _P, _SZ, _P]
         L.hisa_indexer_ev.argtypes = [BP, _P, _I, _I, _P, _I, _I, _P, _P, _P, _SZ, _P, _P, _P]
@@ -269,6 +274,22 @@ def indexer(batch: Batch, pooled, B: int, h: int, k: int, mode: int = 0, heads=N
                                       _ptr(heads), _ptr(head_score), _ptr(idx), _ptr(val),
                                       _ptr(ws), nws, _stream(stream), ctypes.c_void_p(events[0]),
                                       ctypes.c_void_p(events[1])), "misa_indexer_ev")
+    return heads, idx, val
+
+
+def indexer_noalloc(batch: Batch, pooled, B: int, h: int, k: int, mode: int = 0, heads=None,
+                    head_score=None, idx=None, val=None, want_val=True, stream=None):
+    """misa_indexer_noalloc: misa_indexer with the library's static device
+    scratch instead of a workspace (nothing is allocated by the call; the
+    outputs are allocated here only when not passed).  Returns (heads, idx, val)."""
+    torch = _torch()
+    dev = batch.keys.device
+    if heads is None:
+        heads = torch.empty((batch.T, h), dtype=torch.int32, device=dev)
+    idx, val = _sel_out(batch.T, k, dev, idx, val, want_val)
+    _check(load().misa_indexer_noalloc(ctypes.byref(batch.c), _ptr(pooled), B, h, mode, k,
+                                       _ptr(heads), _ptr(head_score), _ptr(idx), _ptr(val),
+                                       _stream(stream)), "misa_indexer_noalloc")
     return heads, idx, val
 
 

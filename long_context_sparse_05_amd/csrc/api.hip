@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "../../include/misa_indexer.h"
 #include "common.hpp"
@@ -258,6 +259,8 @@ const char *misa_status_str(int status) {
     case MISA_ERR_UNSUPPORTED: return "unsupported argument (the library does not handle it)";
     case MISA_ERR_WORKSPACE: return "workspace is smaller than required";
     case MISA_ERR_HIP: return "a HIP launch or runtime call failed";
+    case MISA_ERR_TOO_LARGE:
+      return "the request needs more scratch than the allocation-free call's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -445,16 +448,30 @@ int indexer_dense(const misa_batch *b, int32_t k, int32_t *idx, float *val, void
   return misa_score_topk(b, nullptr, 0, k, idx, val, ws, ws_bytes, stream);
 }
 
-int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t h, int32_t mode,
-                    int32_t k, int32_t *heads, float *head_score, int32_t *idx, float *val,
-                    void *ws, size_t ws_bytes, void *stream, void *ev_start, void *ev_stop) {
+}  // extern "C"
+
+// misa_indexer's checks of everything but the workspace
+static int indexer_check(const misa_batch *b, const float *pooled, int32_t B, int32_t h,
+                         int32_t mode, int32_t k, const int32_t *heads, const int32_t *idx) {
   int rc = check_batch(b, true);
   if (rc) return rc;
-  if (!pooled || !heads || !idx || !ws) return MISA_ERR_NULL;
-  if (!a16(pooled) || !a16(ws)) return MISA_ERR_UNSUPPORTED;
+  if (!pooled || !heads || !idx) return MISA_ERR_NULL;
+  if (!a16(pooled)) return MISA_ERR_UNSUPPORTED;
   if (B < 1 || B > b->Lmax || h < 1 || h > b->H) return MISA_ERR_SHAPE;
   if (mode != 0 && mode != 1) return MISA_ERR_SHAPE;
   if (k < 1 || k > b->Lmax) return MISA_ERR_SHAPE;
+  return MISA_OK;
+}
+
+extern "C" {
+
+int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t h, int32_t mode,
+                    int32_t k, int32_t *heads, float *head_score, int32_t *idx, float *val,
+                    void *ws, size_t ws_bytes, void *stream, void *ev_start, void *ev_stop) {
+  int rc = indexer_check(b, pooled, B, h, mode, k, heads, idx);
+  if (rc) return rc;
+  if (!ws) return MISA_ERR_NULL;
+  if (!a16(ws)) return MISA_ERR_UNSUPPORTED;
   const size_t rbytes = route_bytes(b, B);
   const SelectLayout L = select_layout(b->T, b->Lmax, k, true);
   if (ws_bytes < rbytes + L.total) return MISA_ERR_WORKSPACE;
@@ -487,6 +504,52 @@ int misa_indexer(const misa_batch *b, const float *pooled, int32_t B, int32_t h,
                  size_t ws_bytes, void *stream) {
   return misa_indexer_ev(b, pooled, B, h, mode, k, heads, head_score, idx, val, ws, ws_bytes,
                          stream, nullptr, nullptr);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------- the allocation-free call
+// misa_indexer_noalloc's workspace: a file-scope device array, one copy per
+// GPU, held until the process ends.  Host code never passes `scratch` itself
+// (in host code the name is a host-side stand-in, not a device address): the
+// device address of the current GPU's copy comes from hipGetSymbolAddress,
+// taken once per device on the first call there and kept in scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[MISA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch`, or nullptr on failure.
+void *scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int misa_indexer_noalloc(const misa_batch *b, const float *pooled, int32_t B, int32_t h,
+                         int32_t mode, int32_t k, int32_t *heads, float *head_score, int32_t *idx,
+                         float *val, void *stream) {
+  int rc = indexer_check(b, pooled, B, h, mode, k, heads, idx);
+  if (rc) return rc;
+  size_t need = 0;
+  rc = misa_workspace_bytes(b, MISA_OP_INDEXER, B, h, k, 0, &need);
+  if (rc) return rc;
+  if (need > (size_t)MISA_NOALLOC_SCRATCH_BYTES) return MISA_ERR_TOO_LARGE;
+  void *ws = scratch_address();  // the first HIP call
+  if (!ws) return MISA_ERR_HIP;
+  return misa_indexer_ev(b, pooled, B, h, mode, k, heads, head_score, idx, val, ws,
+                         (size_t)MISA_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr);
 }
 
 int misa_rerank(const misa_batch *b, const int32_t *cand, int32_t kc, int32_t k, int32_t *idx,

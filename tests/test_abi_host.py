@@ -12,7 +12,7 @@ from long_context_sparse_05_amd import abi
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "misa_indexer.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE = 0, -1, -2, -3, -4
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_TOO_LARGE = 0, -1, -2, -3, -4, -6
 
 
 def declared_functions():
@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, -5):
+    for code in (OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, -5, ERR_TOO_LARGE):
         assert abi.status_str(code) and abi.status_str(code) != "unknown status"
     assert abi.status_str(12345) == "unknown status"
 
@@ -84,6 +84,7 @@ def test_workspace_sizes(lib):
 def test_validation_before_any_hip_call(lib):
     P = ctypes.c_void_p
     F = P(FAKE)
+    U16 = P(FAKE + 8)  # aligned to 8, not 16
     big = ctypes.c_size_t(1 << 40)
     b = batch()
     # NULL batch / pointers
@@ -147,6 +148,16 @@ def test_validation_before_any_hip_call(lib):
     assert lib.hisa_indexer(ctypes.byref(b), F, 64, 4, None, 0, 8, F, None, F, small, None) == ERR_WORKSPACE
     assert lib.hisa_blocks(ctypes.byref(b), F, 64, 4, None, 0, F, F, F, small, None) == ERR_WORKSPACE
     assert lib.hisa_blocks(ctypes.byref(b), F, 64, 4, None, 0, F, F, None, big, None) == ERR_NULL
+    # the allocation-free indexer: (b, pooled, B, h, mode, k, heads, head_score, idx, val,
+    # stream); every check, the scratch limit included, comes before any HIP call
+    assert lib.misa_indexer_noalloc(ctypes.byref(b), None, 64, 8, 0, 64, F, None, F, None, None) == ERR_NULL
+    assert lib.misa_indexer_noalloc(ctypes.byref(b), F, 64, 8, 0, 64, None, None, F, None, None) == ERR_NULL
+    assert lib.misa_indexer_noalloc(ctypes.byref(b), F, 64, 9999, 0, 64, F, None, F, None, None) == ERR_SHAPE
+    assert lib.misa_indexer_noalloc(ctypes.byref(b), F, 64, 8, 2, 64, F, None, F, None, None) == ERR_SHAPE
+    assert lib.misa_indexer_noalloc(ctypes.byref(b), U16, 64, 8, 0, 64, F, None, F, None, None) == ERR_UNSUPPORTED
+    huge = batch(S=1, Lmax=1 << 17, T=64, H=8)  # 32 MiB of score rows alone
+    assert lib.misa_indexer_noalloc(ctypes.byref(huge), F, 128, 8, 0, 2048, F, None, F, None,
+                                    None) == ERR_TOO_LARGE
     # base addresses moved in 16-byte vectors must be 16-byte aligned
     U = P(FAKE + 4)
     assert lib.misa_pool(ctypes.byref(batch(keys=FAKE + 4)), 64, F, None) == ERR_UNSUPPORTED
