@@ -246,8 +246,7 @@ int misa_rerank(const misa_batch *b, const int32_t *cand, int32_t kc, int32_t k,
  * (exactly misa_score_topk with those heads) -- Methodology: MISA, both
  * stages.  Outputs as the two calls: heads [T][h] (rank order), head_score
  * [T][H] (may be NULL), idx/val [T][k].  One workspace (MISA_OP_INDEXER with
- * B, h and k) holds both steps' scratch, so the router kernel can also clear
- * the selection histogram and the step needs one launch less.
+ * B, h and k) holds both steps' scratch.
  */
 int misa_indexer(const misa_batch *b, const float *pooled, int32_t B, int32_t h,
                  int32_t mode, int32_t k, int32_t *heads, float *head_score,
@@ -330,6 +329,18 @@ int hisa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t
 int hisa_blocks(const misa_batch *b, const float *pooled, int32_t B, int32_t m,
                 const int32_t *heads, int32_t h, float *block_scores, int32_t *blocks, void *ws,
                 size_t ws_bytes, void *stream);
+
+/*
+ * misa_stream_read -- a plain streaming read of `bytes` of device memory at
+ * `buf`, the bandwidth ceiling the decode roofline is measured against: the
+ * buffer is cut into `wgs` contiguous slices, one workgroup each, read with
+ * the 16-byte non-temporal loads the token-scoring kernel streams keys with.
+ * sink (uint32 [wgs], device) receives one folded word per workgroup (its
+ * value is meaningless).  ev_start / ev_stop: as misa_score_topk_ev (either
+ * may be NULL).  buf and bytes must be 16-byte multiples; 1 <= wgs <= 65535.
+ */
+int misa_stream_read(const void *buf, size_t bytes, int32_t wgs, uint32_t *sink,
+                     void *stream, void *ev_start, void *ev_stop);
 
 /* misa_status_str -- a static English description of a status code. */
 const char *misa_status_str(int status);

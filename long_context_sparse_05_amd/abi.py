@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(HERE, "libmisa_indexer.so")
 EXPORTS = ("misa_workspace_bytes", "misa_pool", "misa_pool_append", "misa_route", "misa_score", "misa_topk",
            "misa_score_topk", "misa_score_topk_ev", "indexer_dense", "misa_rerank",
            "misa_indexer", "misa_indexer_ev", "misa_indexer_noalloc", "hisa_indexer",
-           "hisa_indexer_ev", "hisa_blocks", "misa_status_str")
+           "hisa_indexer_ev", "hisa_blocks", "misa_stream_read", "misa_status_str")
 
 MISA_ERR_TOO_LARGE = -6
 # bytes of misa_indexer_noalloc's static scratch (MISA_NOALLOC_SCRATCH_BYTES)
@@ -70,6 +70,7 @@ def load():
         L.hisa_indexer.argtypes = [BP, _P, _I, _I, _P, _I, _I, _P, _P, _P, _SZ, _P]
         L.hisa_indexer_ev.argtypes = [BP, _P, _I, _I, _P, _I, _I, _P, _P, _P, _SZ, _P, _P, _P]
         L.hisa_blocks.argtypes = [BP, _P, _I, _I, _P, _I, _P, _P, _P, _SZ, _P]
+        L.misa_stream_read.argtypes = [_P, _SZ, _I, _P, _P, _P, _P]
         for name in EXPORTS:
             getattr(L, name).restype = ctypes.c_int
         L.misa_status_str.argtypes = [ctypes.c_int]
@@ -338,6 +339,19 @@ def rerank(batch: Batch, cand, k: int, idx=None, val=None, want_val=True, ws=Non
     _check(load().misa_rerank(ctypes.byref(batch.c), _ptr(cand), kc, k, _ptr(idx), _ptr(val),
                               _ptr(ws), nws, _stream(stream)), "misa_rerank")
     return idx, val
+
+
+def stream_read(buf, wgs: int, sink=None, stream=None, events=None):
+    """misa_stream_read: one plain streaming read of the GPU tensor `buf`
+    (its bytes, a multiple of 16) by `wgs` workgroups; `events` = (start,
+    stop) raw hipEvent_t handles stamped with the kernel's begin and end."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.zeros(wgs, dtype=torch.int32, device=buf.device)
+    ev = (None, None) if events is None else (ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1]))
+    _check(load().misa_stream_read(_ptr(buf), _SZ(buf.numel() * buf.element_size()), wgs, _ptr(sink),
+                                   _stream(stream), *ev), "misa_stream_read")
+    return sink
 
 
 def topk(scores, row_len, k: int, idx=None, val=None, want_val=True, ws=None, stream=None):

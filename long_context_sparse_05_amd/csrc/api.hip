@@ -41,45 +41,55 @@ int check_batch(const misa_batch *b, bool need_q) {
   return MISA_OK;
 }
 
-int hist_chunk(int rows, int ncols) {
-  // about 1024 workgroups; many rows -> whole rows per workgroup, so each
-  // non-empty bin is merged into the row histogram once
+int score_chunk(int rows, int ncols) {
+  // about 512 workgroups over the whole launch (two per CU), 256..4096 columns each
   const size_t work = (size_t)rows * ncols;
-  size_t c = (work + 1023) / 1024;
+  size_t c = (work + 511) / 512;
   c = (c + 255) / 256 * 256;
-  c = std::max<size_t>(4096, std::min<size_t>((size_t)ncols, c));
+  c = std::max<size_t>(256, std::min<size_t>(4096, c));
   return (int)c;
 }
 
-int filter_chunk(int rows, int ncols) {
-  // about 512 filter workgroups, each a multiple of 4096 columns (one round)
-  const int per_row = std::max(1, 512 / std::max(1, rows));
-  int c = (ncols + per_row - 1) / per_row;
-  c = (c + 4095) / 4096 * 4096;
-  return std::max(4096, c);
+// Selection over rows of ld columns.  Few long rows: the two-stage select --
+// [score rows + chunk lists | chunk lists of the given scores] -> merge.
+// Enough rows to fill the GPU, or short rows: [score rows] -> one workgroup
+// per row (topk_rowselect_kernel, after the streamed select for long rows).
+constexpr int kRowSelectMinRows = 256;
+// Rows this short are one workgroup's work whatever their number.
+constexpr int kRowSelectMaxShortRow = 16384;
+
+// The two-stage select takes few long rows whose lists are expected to fit
+// the merge's LDS: about k + nwg (6 sqrt(k / nwg) + 16) entries per row,
+// with room to spare.
+bool list_mode(int rows, int ld, int k) {
+  if (rows >= kRowSelectMinRows || ld <= kRowSelectMaxShortRow) return false;
+  const int cs = score_chunk(rows, ld);
+  const int nwg = std::max((ld + cs - 1) / cs, (ld + kListChunk - 1) / kListChunk);
+  if (nwg > kMaxLists) return false;
+  const double e = (double)k / nwg;
+  return (double)k + nwg * (6.0 * std::sqrt(e) + 17.0) <= 0.85 * 16384.0;
 }
 
 // Layout of the selection workspace for `rows` score rows of `ld` columns:
-// fp32 score rows (when the call computes them), the first-digit histograms
-// and per-row counters (zeroed together by the call), and the per-row
-// threshold-digit candidate lists.
+// fp32 score rows (when the call computes them), per-row counters (the
+// streamed select's flags), and in the two-stage mode the chunk lists
+// (at most ld + 4096 entries per row, whatever the chunk) and their headers.
 struct SelectLayout {
-  size_t scores, hist, counters, cand, total;
-  int cap;
+  size_t scores, counters, lhead, lists, total;
+  bool lists_on;
 };
 SelectLayout select_layout(size_t rows, size_t ld, int k, bool with_scores) {
-  (void)k;
   SelectLayout L;
-  L.cap = (int)std::min<size_t>(ld, 16384);
+  L.lists_on = list_mode((int)std::min<size_t>(rows, 1u << 30), (int)std::min<size_t>(ld, 1u << 30), k);
   size_t off = 0;
   L.scores = off;
   if (with_scores) off = align_up(off + rows * ld * sizeof(float));
-  L.hist = off;
-  off = align_up(off + rows * kHistBins * sizeof(uint32_t));
-  L.counters = off;  // directly after the histograms: one fill clears both
+  L.counters = off;
   off = align_up(off + rows * kRowCounters * sizeof(uint32_t));
-  L.cand = off;
-  off = align_up(off + rows * (size_t)L.cap * sizeof(uint2));
+  L.lhead = off;
+  if (L.lists_on) off = align_up(off + rows * (size_t)kMaxLists * sizeof(uint2));
+  L.lists = off;
+  if (L.lists_on) off = align_up(off + rows * (ld + (size_t)kListChunk) * sizeof(uint2));
   L.total = off;
   return L;
 }
@@ -118,15 +128,6 @@ HisaLayout hisa_layout(const misa_batch *b, int B, int m, int k) {
   return H;
 }
 
-int score_chunk(int rows, int ncols) {
-  // about 512 workgroups over the whole launch (two per CU), 256..4096 columns each
-  const size_t work = (size_t)rows * ncols;
-  size_t c = (work + 511) / 512;
-  c = (c + 255) / 256 * 256;
-  c = std::max<size_t>(256, std::min<size_t>(4096, c));
-  return (int)c;
-}
-
 // Many queries of one sequence with a few routed heads: the dense MFMA
 // tiling of prefill.hip.  Otherwise each query row streams the keys itself.
 constexpr int kPrefillMinRows = 64;
@@ -159,15 +160,6 @@ PrefillArgs make_prefill_args(const misa_batch *b, const int32_t *heads, int h, 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MISA_OK : MISA_ERR_HIP; }
 
-// Selection over rows of ld columns.  Few long rows: zero the histograms ->
-// [score rows + histogram | histogram] -> multi-workgroup filter -> finish.
-// Enough rows to fill the GPU, or short rows: [score rows] -> one workgroup
-// per row.
-constexpr int kRowSelectMinRows = 256;
-// Rows this short are one workgroup's work whatever their number: a single
-// select kernel beats the fill + histogram + filter + finish chain.
-constexpr int kRowSelectMaxShortRow = 16384;
-
 // The streamed select keeps the columns at or above a sampled bracket of
 // the k-th score in a list of kStreamSelectCap entries per row; a row whose
 // list overflows goes on to the row select.  With m = k * sample / ld, the
@@ -185,51 +177,46 @@ bool stream_select_fits(int k, int ld) {
 int run_select(const ScoreArgs *score, const float *scores_in, int rows, int ld,
                const int32_t *row_len, int row_len_add, const int32_t *map, int k,
                int32_t *idx, float *val, void *ws, const SelectLayout &L, hipStream_t st,
-               void *ev_start = nullptr, void *ev_stop = nullptr, bool zeroed = false) {
-  const bool row_mode = rows >= kRowSelectMinRows || ld <= kRowSelectMaxShortRow;
-  uint32_t *hist = (uint32_t *)((char *)ws + L.hist);
+               void *ev_start = nullptr, void *ev_stop = nullptr) {
   hipError_t e = hipSuccess;
-  if (!zeroed && !row_mode) {  // the fused indexer call clears these in its router kernel
-    e = launch_fill_u32(hist, (L.cand - L.hist) / sizeof(uint32_t), 0u, st);
-    if (e != hipSuccess) return MISA_ERR_HIP;
-  }
   TopkArgs t{};
   t.counters = (uint32_t *)((char *)ws + L.counters);
-  t.cand = (uint2 *)((char *)ws + L.cand);
-  t.cap = L.cap;
   t.scores = score ? score->scores : scores_in;
   t.row_len = row_len;
   t.row_len_add = row_len_add;
   t.map = map;
-  t.hist = hist;
   t.idx = idx;
   t.val = val;
   t.rows = rows;
   t.ld = ld;
   t.k = k;
+  if (L.lists_on) {
+    t.lists = (uint2 *)((char *)ws + L.lists);
+    t.lhead = (uint2 *)((char *)ws + L.lhead);
+    t.lcap = score ? score->chunk : kListChunk;
+    t.nwg = (ld + t.lcap - 1) / t.lcap;
+  }
   if (score) {
     ScoreArgs s = *score;
-    s.hist = row_mode ? nullptr : hist;
+    s.lists = t.lists;
+    s.lhead = t.lhead;
+    s.lcap = t.lcap;
+    s.k = k;
     e = launch_score_rows(s, st, (hipEvent_t)ev_start, (hipEvent_t)ev_stop);
     if (e != hipSuccess) return MISA_ERR_HIP;
   }
-  if (row_mode) {
-    // many long rows without a column map: the streamed select, then the
-    // register-resident select on the rows it could not settle
-    if (rows >= kRowSelectMinRows && !map && ld % 4 == 0 && ((uintptr_t)t.scores & 15) == 0 &&
-        ld >= kStreamSelectMinCols && ld <= kStreamSelectMaxCols && stream_select_fits(k, ld)) {
-      if ((e = launch_topk_stream(t, st)) != hipSuccess) return MISA_ERR_HIP;
-      t.only_flagged = 1;
-    }
-    return hip_status(launch_topk_rowselect(t, st));
+  if (L.lists_on) {
+    if (!score && (e = launch_topk_lists(t, st)) != hipSuccess) return MISA_ERR_HIP;
+    return hip_status(launch_topk_merge(t, st));
   }
-  if (!score) {
-    t.chunk = hist_chunk(rows, ld);
-    if ((e = launch_topk_hist(t, hist, st)) != hipSuccess) return MISA_ERR_HIP;
+  // many long rows without a column map: the streamed select, then the
+  // register-resident select on the rows it could not settle
+  if (rows >= kRowSelectMinRows && !map && ld % 4 == 0 && ((uintptr_t)t.scores & 15) == 0 &&
+      ld >= kStreamSelectMinCols && ld <= kStreamSelectMaxCols && stream_select_fits(k, ld)) {
+    if ((e = launch_topk_stream(t, st)) != hipSuccess) return MISA_ERR_HIP;
+    t.only_flagged = 1;
   }
-  t.chunk = filter_chunk(rows, ld);
-  if ((e = launch_topk_select(t, st)) != hipSuccess) return MISA_ERR_HIP;
-  return MISA_OK;
+  return hip_status(launch_topk_rowselect(t, st));
 }
 
 ScoreArgs make_score_args(const misa_batch *b, const int32_t *heads, int nh) {
@@ -354,13 +341,9 @@ static RouteArgs make_route_args(const misa_batch *b, const float *pooled, int32
 // tiled one-kernel router.  Otherwise the per-query partial + final pair,
 // whose final kernel also clears the selection histogram of the fused call.
 constexpr int kRouteTileMinRows = 64;
-hipError_t dispatch_route(const misa_batch *b, const RouteArgs &a, hipStream_t st, bool &zeroed) {
-  if (b->S == 1 && b->T >= kRouteTileMinRows && b->H <= 64) {
-    zeroed = false;
-    return launch_route_tile(a, st);
-  }
-  zeroed = a.zero_hist != nullptr;
-  return launch_route(a, st);
+bool route_tiled(const misa_batch *b) { return b->S == 1 && b->T >= kRouteTileMinRows && b->H <= 64; }
+hipError_t dispatch_route(const misa_batch *b, const RouteArgs &a, hipStream_t st) {
+  return route_tiled(b) ? launch_route_tile(a, st) : launch_route(a, st);
 }
 
 int misa_route(const misa_batch *b, const float *pooled, int32_t B, int32_t h, int32_t mode,
@@ -373,8 +356,7 @@ int misa_route(const misa_batch *b, const float *pooled, int32_t B, int32_t h, i
   if (mode != 0 && mode != 1) return MISA_ERR_SHAPE;
   if (ws_bytes < route_bytes(b, B)) return MISA_ERR_WORKSPACE;
   const RouteArgs a = make_route_args(b, pooled, B, h, mode, heads, head_score, ws);
-  bool zeroed;
-  return hip_status(dispatch_route(b, a, (hipStream_t)stream, zeroed));
+  return hip_status(dispatch_route(b, a, (hipStream_t)stream));
 }
 
 int misa_score(const misa_batch *b, const int32_t *heads, int32_t h, float *scores,
@@ -389,7 +371,6 @@ int misa_score(const misa_batch *b, const int32_t *heads, int32_t h, float *scor
                                            (hipStream_t)stream));
   ScoreArgs s = make_score_args(b, heads, heads ? h : b->H);
   s.scores = scores;
-  s.hist = nullptr;
   s.cand = nullptr;
   s.ncols = b->Lmax;
   s.ld = b->Lmax;
@@ -476,27 +457,40 @@ int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t
   const SelectLayout L = select_layout(b->T, b->Lmax, k, true);
   if (ws_bytes < rbytes + L.total) return MISA_ERR_WORKSPACE;
   void *sws = (char *)ws + rbytes;
-  RouteArgs ra = make_route_args(b, pooled, B, h, mode, heads, head_score, ws);
-  ra.zero_hist = (uint32_t *)((char *)sws + L.hist);
-  ra.zero_ctr = (uint32_t *)((char *)sws + L.counters);
-  bool zeroed;
-  if (dispatch_route(b, ra, (hipStream_t)stream, zeroed) != hipSuccess) return MISA_ERR_HIP;
-  if (use_prefill(b, heads, h)) {
+  const RouteArgs ra = make_route_args(b, pooled, B, h, mode, heads, head_score, ws);
+  // many queries of one sequence: the tiled router writes the heads; the
+  // prefill tiling reads them from memory; otherwise the router kernel
+  // leaves partial sums that the scoring kernel's prologue reduces and ranks
+  const bool tiled_router = route_tiled(b), prefill = use_prefill(b, heads, h);
+  const bool in_prologue = !tiled_router && !prefill;
+  hipError_t re = tiled_router ? launch_route_tile(ra, (hipStream_t)stream)
+                  : prefill    ? launch_route(ra, (hipStream_t)stream)
+                               : launch_route_partial(ra, (hipStream_t)stream);
+  if (re != hipSuccess) return MISA_ERR_HIP;
+  if (prefill) {
     float *sc = (float *)((char *)sws + L.scores);
     if (launch_score_prefill(make_prefill_args(b, heads, h, sc), (hipStream_t)stream,
                              (hipEvent_t)ev_start, (hipEvent_t)ev_stop) != hipSuccess)
       return MISA_ERR_HIP;
     return run_select(nullptr, sc, b->T, b->Lmax, b->q_pos, 1, nullptr, k, idx, val, sws, L,
-                      (hipStream_t)stream, nullptr, nullptr, zeroed);
+                      (hipStream_t)stream);
   }
   ScoreArgs s = make_score_args(b, heads, h);
+  if (in_prologue) {  // heads come from the router's partial sums
+    s.heads = nullptr;
+    s.partial = ra.partial;
+    s.nparts = ra.nchunks + 1;
+    s.mode = mode;
+    s.heads_out = heads;
+    s.g_out = head_score;
+  }
   s.scores = (float *)((char *)sws + L.scores);
   s.cand = nullptr;
   s.ncols = b->Lmax;
   s.ld = b->Lmax;
   s.chunk = score_chunk(b->T, b->Lmax);
   return run_select(&s, nullptr, b->T, b->Lmax, b->q_pos, 1, nullptr, k, idx, val, sws, L,
-                    (hipStream_t)stream, ev_start, ev_stop, zeroed);
+                    (hipStream_t)stream, ev_start, ev_stop);
 }
 
 int misa_indexer(const misa_batch *b, const float *pooled, int32_t B, int32_t h, int32_t mode,

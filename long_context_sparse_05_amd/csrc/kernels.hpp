@@ -24,7 +24,20 @@ struct ScoreArgs {
   int32_t *cand_out;
   int nkept, blk;
   float *scores;           // [T][ld]
-  uint32_t *hist;          // [T][4096] first-digit histogram (accumulated), or nullptr
+  // Chunk candidate lists for the two-stage top-k (select.hpp), or nullptr:
+  // workgroup x of row t writes list [t][x][lcap] and its header [t][x]
+  // (entries, cutoff digit), keeping its share of the row's top k.
+  uint2 *lists;
+  uint2 *lhead;
+  int lcap, k;
+  // The router's partial sums [T][nparts][H] (route_partial_kernel), or
+  // nullptr: the prologue then reduces and ranks them (route_finish.hpp)
+  // into the nh routed heads instead of reading `heads`; workgroup 0 of
+  // each row writes them to heads_out [T][nh] and g to g_out [T][H].
+  const float *partial;
+  int nparts, mode;
+  int32_t *heads_out;
+  float *g_out;
   int nh, H, Lmax, T;
   int ncols, ld, chunk;
 };
@@ -60,24 +73,27 @@ struct TopkArgs {
   const int32_t *row_len;  // [rows] or nullptr (all ld columns)
   int row_len_add;         // valid columns = row_len[r] + row_len_add
   const int32_t *map;      // [rows][ld] column -> token id (-1 = empty) or nullptr
-  const uint32_t *hist;    // [rows][4096] first-digit histogram of the valid columns
   uint32_t *counters;      // [rows][kRowCounters] (select.hpp)
-  uint2 *cand;             // [rows][cap] threshold-digit candidates (order key, column)
-  int cap;                 // <= 16384
+  // the rows' chunk candidate lists [rows][nwg][lcap] and headers [rows][nwg]
+  // (two-stage top-k of few long rows: topk_merge_kernel)
+  uint2 *lists;
+  uint2 *lhead;
+  int nwg, lcap;
   int32_t *idx;            // [rows][k]
   float *val;              // [rows][k] or nullptr
-  int rows, ld, k, chunk;  // chunk: columns per workgroup (histogram / filter)
+  int rows, ld, k;
   int only_flagged;        // row select: skip rows whose counter 7 is 0 (streamed select done)
 };
-hipError_t launch_topk_hist(const TopkArgs &a, uint32_t *hist, hipStream_t st);
-hipError_t launch_topk_select(const TopkArgs &a, hipStream_t st);
+constexpr int kMaxLists = 1024;   // chunk lists per row the merge takes
+constexpr int kListChunk = 4096;  // columns per workgroup of topk_lists_kernel
+hipError_t launch_topk_merge(const TopkArgs &a, hipStream_t st);
+hipError_t launch_topk_lists(const TopkArgs &a, hipStream_t st);
 hipError_t launch_topk_rowselect(const TopkArgs &a, hipStream_t st);
 hipError_t launch_topk_stream(const TopkArgs &a, hipStream_t st);  // then the row select on flagged rows
 constexpr int kStreamSelectMinCols = 16384;   // rows of kStreamSelectMinCols..kStreamSelectMaxCols
 constexpr int kStreamSelectMaxCols = 131072;  // columns take the streamed select
 constexpr int kStreamSelectCap = 4096;        // its list of bracketed columns, per row
 constexpr int kStreamSelectSample = 4096;     // its sample, per row
-hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t st);
 
 // Block mean-pool (pool.hip).
 hipError_t launch_pool(const uint16_t *keys, const int32_t *seq_lens, int S, int Lmax,
@@ -97,8 +113,6 @@ struct RouteArgs {
   float *partial;          // [T][nchunks + 1][H]
   int32_t *heads;          // [T][h]
   float *g;                // [T][H] or nullptr
-  uint32_t *zero_hist;     // [T][4096] zeroed by route_final (fused indexer call), or nullptr
-  uint32_t *zero_ctr;      // [T][8] zeroed with it
   int S, Lmax, T, H, B, h, mode, Mmax, nchunks;
 };
 constexpr int kRouteChunk = 64;  // complete blocks per router workgroup
@@ -118,6 +132,9 @@ struct HisaArgs {
 };
 hipError_t launch_hisa_blocks(const HisaArgs &a, hipStream_t st);
 hipError_t launch_route(const RouteArgs &a, hipStream_t st);
+// the partial sums alone: the fused indexer call ranks the heads in the
+// scoring kernel's prologue (ScoreArgs::partial)
+hipError_t launch_route_partial(const RouteArgs &a, hipStream_t st);
 // many queries of one sequence, H <= 64: one kernel, heads written directly
 hipError_t launch_route_tile(const RouteArgs &a, hipStream_t st);
 

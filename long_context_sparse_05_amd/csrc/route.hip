@@ -20,6 +20,7 @@
 // applies the weight and selects the top-h heads by (g desc, head id asc).
 #include "common.hpp"
 #include "kernels.hpp"
+#include "route_finish.hpp"
 
 namespace misa {
 
@@ -187,65 +188,15 @@ __global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a) {
   for (int j = tid; j < a.H; j += 256) out[j] = ((part[0][j] + part[1][j]) + part[2][j]) + part[3][j];
 }
 
-// One workgroup per query: four thread quarters sum contiguous quarters of
-// the partials (loads in flight together), combined in a fixed order; then
-// every head computes its own rank, and ranks below h are written.  In the
-// fused indexer call it also clears the query's selection histogram, which
-// saves the scoring step a separate fill launch.
+// One workgroup per query: the partial sums reduced in a fixed order,
+// weighted and ranked (route_finish.hpp).
 __global__ __launch_bounds__(256) void route_final_kernel(RouteArgs a) {
   __shared__ float red[4][MISA_MAX_HEADS_DEV];
   __shared__ float gs[MISA_MAX_HEADS_DEV];
   const int t = blockIdx.x;
-  const int tid = threadIdx.x, lane = lane_id(), quarter = tid >> 6;
   const int nparts = a.nchunks + 1;
-  const float *pp = a.partial + (size_t)t * nparts * a.H;
-  const int per = (nparts + 3) / 4;
-  const int c0 = quarter * per, c1 = min(nparts, c0 + per);
-  if (a.zero_hist) {  // fused indexer call: clear this query's selection histogram
-    uint4 *zh = (uint4 *)(a.zero_hist + (size_t)t * kHistBins);
-    for (int i = tid; i < kHistBins / 4; i += 256) zh[i] = make_uint4(0, 0, 0, 0);
-    if (tid < 8) a.zero_ctr[(size_t)t * 8 + tid] = 0u;
-  }
-  // this thread's head weight (clamped index, used for tid < H), requested
-  // with the partials: batches of eight in flight, from clamped indices, the
-  // ones past the quarter masked to +0 (no branch around a load), added in
-  // order; the second 64 heads only when H > 64
-  const float wpre = a.w[(size_t)t * a.H + min(tid, a.H - 1)];
-  for (int u = 0; u < 2 && 64 * u < a.H; ++u) {
-    const int j = lane + 64 * u;
-    const float *pj = pp + min(j, a.H - 1);
-    float s = 0.f;
-    for (int c = c0; c < c1; c += 8) {
-      float v[8];
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const uint32_t m = c + x < c1 ? 0xFFFFFFFFu : 0u;
-        v[x] = __uint_as_float(__float_as_uint(pj[(size_t)min(c + x, c1 - 1) * a.H]) & m);
-      }
-#pragma unroll
-      for (int x = 0; x < 8; ++x) s += v[x];
-    }
-    if (j < a.H) red[quarter][j] = s;
-  }
-  __syncthreads();
-  if (tid < a.H) {
-    const float s = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
-    float wj = wpre;
-    if (a.mode == 1) wj = fabsf(wj);
-    gs[tid] = wj * s;
-    if (a.g) a.g[(size_t)t * a.H + tid] = gs[tid];
-  }
-  __syncthreads();
-  // rank of head j under (g desc, id asc); the heads of rank < h are routed
-  if (tid < a.H) {
-    const float gj = gs[tid];
-    int rank = 0;
-    for (int i = 0; i < a.H; ++i) {
-      const float gi = gs[i];
-      rank += (gi > gj || (gi == gj && i < tid)) ? 1 : 0;
-    }
-    if (rank < a.h) a.heads[(size_t)t * a.h + rank] = tid;
-  }
+  route_finish(a.partial + (size_t)t * nparts * a.H, nparts, a.H, a.w + (size_t)t * a.H, a.mode, a.h,
+               red, gs, a.g ? a.g + (size_t)t * a.H : nullptr, a.heads + (size_t)t * a.h, nullptr);
 }
 
 // ------------------------------------------------------------ tile router
@@ -519,12 +470,16 @@ static void launch_partial(const RouteArgs &a, hipStream_t st) {
   hipLaunchKernelGGL((route_partial_kernel<HT>), dim3(a.nchunks + 1, a.T), dim3(256), 0, st, a);
 }
 
-hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
+hipError_t launch_route_partial(const RouteArgs &a, hipStream_t st) {
   if (a.H <= 16) launch_partial<1>(a, st);
   else if (a.H <= 32) launch_partial<2>(a, st);
   else if (a.H <= 64) launch_partial<4>(a, st);
   else launch_partial<8>(a, st);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
+  hipError_t e = launch_route_partial(a, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(route_final_kernel, dim3(a.T), dim3(256), 0, st, a);
   return hipGetLastError();

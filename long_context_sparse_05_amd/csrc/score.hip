@@ -21,30 +21,47 @@
 // of 32 consecutive columns at once.  The scores of the workgroup's chunk
 // collect in LDS and leave in one burst of 16-byte stores at the end: score
 // stores spread through the key stream cost more HBM time than their bytes.
-// The epilogue also builds a 4096-bin histogram of the top 12 bits of each
-// score's order key, the first radix digit of the per-row top-k.
+// For the top-k of few long rows the epilogue also keeps the chunk's
+// candidate list: a 4096-bin LDS histogram of the top 12 bits of each
+// score's order key gives the cutoff digit of the chunk's share of the row's
+// top k, and the entries at or above it are written out (select.hpp).
 #include <hip/hip_ext.h>
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "route_finish.hpp"
+#include "select.hpp"
 
 namespace misa {
 
 constexpr int kKeyRowLds = 272;  // bytes per key row in the LDS tile (256 + 16)
+// Waves per workgroup: eight where one 16-row head tile keeps a wave within
+// 128 registers (two workgroups, sixteen waves, per CU: more key loads in
+// flight), four otherwise.
+template <int HT, bool GATHER>
+constexpr int score_waves() {
+  return HT == 1 && !GATHER ? 8 : 4;
+}
 
-template <int HT, bool GATHER, int U>
-__global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
+template <int HT, bool GATHER, bool ROUTE, int U, int NW>
+__global__ __launch_bounds__(NW * 64) void score_rows_kernel(ScoreArgs a) {
+  constexpr int NT = NW * 64;
+  static_assert(!(ROUTE && GATHER), "the router prologue serves direct rows");
   __shared__ uint32_t lds_hist[kHistBins];
-  __shared__ uint4 tile[4][16 * kKeyRowLds / 16];
+  __shared__ float rred[ROUTE ? 4 : 1][MISA_MAX_HEADS_DEV];  // router prologue scratch
+  __shared__ float rgs[ROUTE ? MISA_MAX_HEADS_DEV : 1];
+  __shared__ int32_t rheads[ROUTE ? MISA_MAX_HEADS_DEV : 1];  // the routed heads
+  __shared__ uint4 tile[NW][16 * kKeyRowLds / 16];
   __shared__ int32_t ctok[GATHER ? kMaxScoreChunk : 1];  // the chunk's candidate tokens
   __shared__ float csc[kMaxScoreChunk];                   // the chunk's scores
+  __shared__ uint32_t lsh[16];                            // scan scratch, valid-entry count
   const int t = blockIdx.y;
   const int lane = lane_id();
   // wave-uniform, and known to be: the step loop below branches on scalars
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;   // MFMA column (key) / 16-byte slice of a key row
   const int grp = lane >> 4;   // lane group: k sub-slice / accumulator rows / key of a load
-  const bool hist = a.hist != nullptr;
+  const bool lists = a.lists != nullptr;
 
   const int c0 = blockIdx.x * a.chunk;
   const int c1 = min(c0 + a.chunk, a.ncols);
@@ -53,18 +70,28 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
   const int nvalid = GATHER ? a.ncols : min(a.ncols, a.q_pos[t] + 1);
   float *srow = a.scores + (size_t)t * a.ld;
 
-  if (hist) {
-    for (int b = threadIdx.x; b < kHistBins; b += 256) lds_hist[b] = 0;
+  if (lists) {
+    for (int b = threadIdx.x; b < kHistBins; b += NT) lds_hist[b] = 0;
+    if (threadIdx.x == 0) lsh[15] = 0;
+    if (GATHER) __syncthreads();  // the count is zero before the candidate loop adds to it
   }
   if (!GATHER && c0 >= nvalid) {  // uniform across the workgroup: no barrier follows
-    for (int c = c0 + threadIdx.x; c < c1; c += 256) srow[c] = -INFINITY;
+    for (int c = c0 + threadIdx.x; c < c1; c += NT) srow[c] = -INFINITY;
+    if (lists && threadIdx.x == 0) a.lhead[(size_t)t * gridDim.x + blockIdx.x] = make_uint2(0u, 0u);
     return;
+  }
+
+  const size_t seq_base = (size_t)a.q_seq[t] * a.Lmax;
+  if constexpr (ROUTE) {  // the router's last step: reduce the partials, rank the heads
+    route_finish(a.partial + (size_t)t * a.nparts * a.H, a.nparts, a.H, a.w + (size_t)t * a.H, a.mode,
+                 a.nh, rred, rgs, (blockIdx.x == 0 && a.g_out) ? a.g_out + (size_t)t * a.H : nullptr,
+                 blockIdx.x == 0 ? a.heads_out + (size_t)t * a.nh : nullptr, rheads);
+    __syncthreads();
   }
 
   // Query head fragments (A operand) and the weights of this lane's rows:
   // two batched rounds of loads (head ids, then rows and weights), indices
   // clamped and rows past nh masked, so that no load waits behind a branch
-  const size_t seq_base = (size_t)a.q_seq[t] * a.Lmax;
   bf16x8 qa[HT][4];
   float wv[HT][4];
   {
@@ -72,11 +99,11 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       const int m = min(ht * 16 + col, a.nh - 1);
-      jq[ht] = a.heads ? a.heads[(size_t)t * a.nh + m] : m;
+      jq[ht] = ROUTE ? rheads[m] : a.heads ? a.heads[(size_t)t * a.nh + m] : m;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int mr = min(ht * 16 + grp * 4 + r, a.nh - 1);
-        jw[ht][r] = a.heads ? a.heads[(size_t)t * a.nh + mr] : mr;
+        jw[ht][r] = ROUTE ? rheads[mr] : a.heads ? a.heads[(size_t)t * a.nh + mr] : mr;
       }
     }
 #pragma unroll
@@ -99,19 +126,27 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
       const int32_t *krow = a.kept + (size_t)t * a.nkept;
       int32_t *orow = a.cand_out + (size_t)t * a.ncols;
       const int p = a.q_pos[t];
-      for (int c = c0 + threadIdx.x; c < c1; c += 256) {
+      uint32_t nv = 0;
+      for (int c = c0 + threadIdx.x; c < c1; c += NT) {
         const int i = c / a.blk, b = krow[i], tok = b * a.blk + (c - i * a.blk);
         const int v = (b >= 0 && tok <= p) ? tok : -1;
         ctok[c - c0] = v;
         orow[c] = v;
+        nv += v >= 0 ? 1u : 0u;
       }
+      if (lists && nv) atomicAdd(&lsh[15], nv);
     } else {
       const int32_t *crow = a.cand + (size_t)t * a.ncols;
-      for (int c = c0 + threadIdx.x; c < c1; c += 256) ctok[c - c0] = crow[c];
+      uint32_t nv = 0;
+      for (int c = c0 + threadIdx.x; c < c1; c += NT) {
+        const int v = crow[c];
+        ctok[c - c0] = v;
+        nv += v >= 0 ? 1u : 0u;
+      }
+      if (lists && nv) atomicAdd(&lsh[15], nv);
     }
   }
-  if (hist || GATHER) __syncthreads();
-
+  if (lists || GATHER) __syncthreads();
   char *wt = (char *)tile[wave];
   // U tiles of 16 keys per step; load i of tile u covers keys 4i..4i+3
   // Every load is issued unconditionally, from a column clamped into
@@ -134,6 +169,14 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
       for (int i = 0; i < 4; ++i)
         kv[u][i] = load_nt16(a.keys + (seq_base + (size_t)tok[u][i]) * kD + col * 8);
   };
+  const int stride = NW * 16 * U;
+  const int wstart = c0 + wave * 16 * U;
+  const int nsteps = wstart < c1 ? (c1 - wstart + stride - 1) / stride : 0;
+  uint4 ka[U][4], kb2[U][4];
+  // with the router's last step in the prologue, the first step's keys are
+  // requested before the heads are known (their loads overlap the reduction)
+
+
   auto process_step = [&](int base, const uint4 (&kv)[U][4]) {
     float part[U];
 #pragma unroll
@@ -168,7 +211,7 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
       const bool ok = c < nvalid && (!GATHER || ctok[c - c0] >= 0);
       const float sc = ok ? own : -INFINITY;
       csc[c - c0] = sc;
-      if (hist && ok) atomicAdd(&lds_hist[order_key(sc) >> kHistShift], 1u);
+      if (lists && ok) atomicAdd(&lds_hist[order_key(sc) >> kHistShift], 1u);
     }
   };
   // software pipeline over two register buffers: the next step's loads are
@@ -176,10 +219,6 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
   // Every path that goes on has issued the next step's loads (the last
   // steps leave the loop), so the compiler waits only for the step it
   // processes.
-  const int stride = 4 * 16 * U;
-  const int wstart = c0 + wave * 16 * U;
-  const int nsteps = wstart < c1 ? (c1 - wstart + stride - 1) / stride : 0;
-  uint4 ka[U][4], kb2[U][4];
   if (nsteps > 0) {
     load_step(wstart, ka);
     for (int st = 0;; st += 2) {
@@ -198,48 +237,53 @@ __global__ __launch_bounds__(256) void score_rows_kernel(ScoreArgs a) {
       process_step(b0 + stride, kb2);
     }
   }
-  // the chunk's scores, in 16-byte non-temporal stores where aligned
   __syncthreads();
+  if (lists) {  // the chunk's share of the row's top k, for the merge (before the
+    // score stores: work after them would wait for the stores to land)
+    const uint32_t nvc = GATHER ? lsh[15] : (uint32_t)max(0, min(c1, nvalid) - c0);
+    const uint32_t quota = chunk_quota(a.k, (int)nvc, nvalid);
+    const uint32_t cap = min((uint32_t)a.lcap, 2u * quota + 64u);
+    const size_t slot = (size_t)t * gridDim.x + blockIdx.x;
+    chunk_list<NT, kMaxScoreChunk / NT>(
+        csc, c1 - c0, lds_hist, nvc, quota, cap,
+        [&](int i) { return GATHER ? ctok[i] >= 0 : c0 + i < nvalid; },
+        [&](int i) { return GATHER ? ctok[i] : c0 + i; }, a.lists + slot * a.lcap, a.lhead + slot, lsh);
+  }
+  // the chunk's scores, in 16-byte non-temporal stores where aligned
   {
     const int n = c1 - c0;
     if ((n & 3) == 0 && (((size_t)t * a.ld + c0) & 3) == 0) {
-      for (int i = threadIdx.x * 4; i < n; i += 1024) {
+      for (int i = threadIdx.x * 4; i < n; i += 4 * NT) {
         const float4 v = *(const float4 *)&csc[i];
         __builtin_nontemporal_store((f32x4){v.x, v.y, v.z, v.w}, (f32x4 *)(srow + c0 + i));
       }
     } else {
-      for (int i = threadIdx.x; i < n; i += 256) srow[c0 + i] = csc[i];
-    }
-  }
-  if (hist) {
-    __syncthreads();
-    uint32_t *grow = a.hist + (size_t)t * kHistBins;
-    for (int b = threadIdx.x; b < kHistBins; b += 256) {
-      const uint32_t v = lds_hist[b];
-      if (v) atomicAdd(&grow[b], v);
+      for (int i = threadIdx.x; i < n; i += NT) srow[c0 + i] = csc[i];
     }
   }
 }
 
-template <int HT, bool GATHER>
+template <int HT, bool GATHER, bool ROUTE>
 static hipError_t launch_ht(const ScoreArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   dim3 grid((a.ncols + a.chunk - 1) / a.chunk, a.T);
   // two 16-key tiles per wave step: fewer registers, more waves per CU
   constexpr int U = 2;
+  constexpr int NW = score_waves<HT, GATHER>();
   if (a.chunk > kMaxScoreChunk) return hipErrorInvalidValue;
   if (ev0 || ev1)  // the measurement hook: events stamped with the kernel's begin and end
-    hipExtLaunchKernelGGL((score_rows_kernel<HT, GATHER, U>), grid, dim3(256), 0, st, ev0, ev1, 0, a);
+    hipExtLaunchKernelGGL((score_rows_kernel<HT, GATHER, ROUTE, U, NW>), grid, dim3(NW * 64), 0, st, ev0, ev1,
+                          0, a);
   else
-    hipLaunchKernelGGL((score_rows_kernel<HT, GATHER, U>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((score_rows_kernel<HT, GATHER, ROUTE, U, NW>), grid, dim3(NW * 64), 0, st, a);
   return hipGetLastError();
 }
 
-template <bool GATHER>
+template <bool GATHER, bool ROUTE>
 static hipError_t launch_g(const ScoreArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  if (a.nh <= 16) return launch_ht<1, GATHER>(a, st, ev0, ev1);
-  if (a.nh <= 32) return launch_ht<2, GATHER>(a, st, ev0, ev1);
-  if (a.nh <= 64) return launch_ht<4, GATHER>(a, st, ev0, ev1);
-  return launch_ht<8, GATHER>(a, st, ev0, ev1);
+  if (a.nh <= 16) return launch_ht<1, GATHER, ROUTE>(a, st, ev0, ev1);
+  if (a.nh <= 32) return launch_ht<2, GATHER, ROUTE>(a, st, ev0, ev1);
+  if (a.nh <= 64) return launch_ht<4, GATHER, ROUTE>(a, st, ev0, ev1);
+  return launch_ht<8, GATHER, ROUTE>(a, st, ev0, ev1);
 }
 
 hipError_t launch_score_rows(const ScoreArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
@@ -248,7 +292,11 @@ hipError_t launch_score_rows(const ScoreArgs &a, hipStream_t st, hipEvent_t ev0,
     if (ev1 && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;
     return hipSuccess;
   }
-  return (a.cand || a.kept) ? launch_g<true>(a, st, ev0, ev1) : launch_g<false>(a, st, ev0, ev1);
+  if (a.partial) {  // the fused indexer call: the router's last step in the prologue
+    if (a.cand || a.kept || !a.heads_out || a.nh > a.H) return hipErrorInvalidValue;
+    return launch_g<false, true>(a, st, ev0, ev1);
+  }
+  return (a.cand || a.kept) ? launch_g<true, false>(a, st, ev0, ev1) : launch_g<false, false>(a, st, ev0, ev1);
 }
 
 }  // namespace misa

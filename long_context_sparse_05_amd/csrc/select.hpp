@@ -90,4 +90,63 @@ __device__ __forceinline__ Thresh threshold_from_lds(const uint32_t *lh, uint32_
   return th;
 }
 
+// ------------------------------------------------------- chunk candidate lists
+// The two-stage top-k of few long rows.  A row is cut into chunks (one per
+// workgroup of the kernel that produces its scores); each chunk keeps a
+// short list of its best entries -- every valid entry whose 12-bit digit is
+// at least a cutoff `cut` -- and records the cutoff, so that every entry it
+// dropped has a digit below `cut`.  The row's top-k is then exact if it is
+// taken from the union of the lists and its k-th key has a digit no lower
+// than every chunk's cutoff (topk_merge_kernel checks this, and otherwise
+// selects from the whole score row).
+//
+// A chunk of n columns out of a row of n_row valid columns holds, on
+// average, E = k n / n_row of the row's top k; it keeps its best
+// quota = E + 6 sqrt(E) + 16 entries (rounded up to whole digits), so a
+// chunk holding more of the row's top-k than that -- which makes the check
+// fail -- is a six-sigma event on unstructured scores.
+__device__ __forceinline__ uint32_t chunk_quota(int k, int n, int n_row) {
+  if (n_row <= 0) return 0u;
+  const float e = (float)k * (float)n / (float)n_row;
+  const float q = ceilf(e + 6.f * sqrtf(e) + 16.f);
+  return q >= (float)n ? (uint32_t)n : (uint32_t)q;
+}
+
+// List entry: (order key, token id); header: (entries, cutoff digit).
+// sc: the chunk's n scores in LDS; lh: the 4096-bin histogram of the top 12
+// key bits of its nvalid valid entries (LDS); valid(i) / tok(i): entry i's
+// validity and token id.  Every thread of the NT-thread workgroup calls this
+// with uniform arguments (it contains barriers).  At most cap entries are
+// written to out.
+template <int NT, int MAXPER, typename Valid, typename Tok>
+__device__ __forceinline__ void chunk_list(const float *sc, int n, const uint32_t *lh, uint32_t nvalid,
+                                           uint32_t quota, uint32_t cap, Valid valid, Tok tok, uint2 *out,
+                                           uint2 *head, uint32_t *sh) {
+  const int tid = threadIdx.x;
+  uint32_t cut = 0;  // keep every valid entry
+  if (quota < nvalid) {
+    const Thresh th = threshold_from_lds<NT>(lh, quota, sh);
+    // the digit holding the quota-th best entry, or the one above it when
+    // that digit's entries would overflow the list
+    cut = th.above + th.eq <= cap ? (uint32_t)th.b1 : (uint32_t)th.b1 + 1u;
+  }
+  uint32_t hits = 0;
+#pragma unroll
+  for (int u = 0; u < MAXPER; ++u) {
+    const int i = tid + NT * u;
+    if (i < n && valid(i) && (order_key(sc[i]) >> kHistShift) >= cut) hits |= 1u << u;
+  }
+  uint32_t total;
+  uint32_t pos = block_scan<NT>((uint32_t)__popc(hits), sh, total) - (uint32_t)__popc(hits);
+#pragma unroll
+  for (int u = 0; u < MAXPER; ++u) {
+    if ((hits >> u) & 1u) {
+      const int i = tid + NT * u;
+      if (pos < cap) out[pos] = make_uint2(order_key(sc[i]), (uint32_t)tok(i));
+      ++pos;
+    }
+  }
+  if (tid == 0) *head = make_uint2(min(total, cap), total <= cap ? cut : 0xFFFFFFFFu);
+}
+
 }  // namespace misa

@@ -7,22 +7,24 @@
 // key (order_key(score) << 32) | ~token: keys are unique and their order is
 // exactly the ranking, so the top-k is "every key >= the k-th largest key".
 //
-//  1. a 4096-bin histogram of the top 12 key bits, accumulated into the
-//     workspace by the scoring kernel's epilogue (or topk_hist_kernel for
-//     caller-provided scores);
-//  2. topk_filter_kernel, many workgroups per row: the digit b1 holding the
-//     kk-th key comes from the histogram; columns above b1 go straight to
-//     the output and columns equal to b1 (the candidates) to a per-row list.
-//     Positions within a workgroup come from a block-wide scan, and ONE
-//     global atomic per counter per 4096 columns reserves the workgroup's
-//     range (same-address global atomics serialise: per-element or per-wave
-//     atomics from hundreds of workgroups would dominate);
-//  3. topk_finish_kernel, one 1024-thread workgroup per row: the candidates
-//     are loaded into LDS and the remaining 52 key bits resolved with 8-bit
-//     digit passes over LDS histograms, emitting every key above each pass's
-//     crossing digit and compacting the survivors, until the crossing bin
-//     holds exactly the keys still needed.  More than 16384 candidates
-//     (heavy ties) are re-read from the score row instead.
+// Few long rows (decode: a handful of queries, 32K..128K columns each) take
+// two stages:
+//  1. each chunk of a row -- the columns one workgroup of the scoring kernel
+//     produced, or of topk_lists_kernel for caller-provided scores -- keeps
+//     a list of its best entries, every valid entry whose top 12 key bits
+//     are at least a cutoff digit chosen from an LDS histogram of the chunk
+//     so that the list holds a little more than the chunk's expected share
+//     of the row's top-k (select.hpp, chunk_list);
+//  2. topk_merge_kernel, one 1024-thread workgroup per row, loads the
+//     union of the lists into LDS, takes its exact top-k (12-bit digit
+//     histogram, then 8-bit digit passes over the threshold digit's keys)
+//     and checks that the k-th key's digit is no lower than every chunk's
+//     cutoff, which proves no dropped entry belongs in the top-k; if the
+//     check fails (a chunk holds far more than its share, heavy ties) the
+//     same workgroup runs the exact row select over the row's scores.
+// Many rows, or short rows: one workgroup per row (topk_rowselect_kernel),
+// or for rows of 16K..128K columns first the streamed select of
+// topk_stream_kernel.
 #include <type_traits>
 
 #include "common.hpp"
@@ -34,6 +36,17 @@ namespace misa {
 constexpr int kSelThreads = 1024;
 constexpr int kSelCap = 16384;      // candidates resolved in LDS (128 KiB)
 constexpr int kSelCompact = 2048;   // survivors compacted after each pass
+
+// The LDS of a 1024-thread row select, declared once by each kernel that
+// runs one (the merge kernel reuses it, so its fallback to the exact row
+// select needs no second copy).
+struct SelLds {
+  uint64_t cs[kSelCap];
+  uint64_t cs2[kSelCompact];
+  uint32_t hs[256];
+  uint32_t sh[kSelThreads / kWave + 16];
+  unsigned long long cnt64;
+};
 
 __device__ __forceinline__ int row_valid_len(const TopkArgs &a, int r) {
   return a.row_len ? max(0, min(a.ld, a.row_len[r] + a.row_len_add)) : a.ld;
@@ -53,148 +66,6 @@ __device__ __forceinline__ bool lds_append(bool pred, uint32_t *counter, uint32_
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, int tok) {
   return ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)tok);
-}
-
-// ---------------------------------------------------------------- histogram
-__global__ __launch_bounds__(256) void topk_hist_kernel(TopkArgs a, uint32_t *hist) {
-  __shared__ uint32_t h[kHistBins];
-  const int r = blockIdx.y;
-  for (int b = threadIdx.x; b < kHistBins; b += 256) h[b] = 0;
-  __syncthreads();
-  const int n = row_valid_len(a, r);
-  const int c0 = blockIdx.x * a.chunk, c1 = min(c0 + a.chunk, n);
-  const float *srow = a.scores + (size_t)r * a.ld;
-  for (int c = c0 + threadIdx.x; c < c1; c += 256) {
-    if (a.map && a.map[(size_t)r * a.ld + c] < 0) continue;
-    atomicAdd(&h[order_key(srow[c]) >> kHistShift], 1u);
-  }
-  __syncthreads();
-  for (int b = threadIdx.x; b < kHistBins; b += 256)
-    if (h[b]) atomicAdd(&hist[(size_t)r * kHistBins + b], h[b]);
-}
-
-// ------------------------------------------------------------------- filter
-// Positions come from one block-wide scan per round of 4096 columns, and the
-// results go to this workgroup's own slots: no atomics and no staging
-// buffers, so several workgroups fit on a CU.
-template <bool MAP>
-__global__ __launch_bounds__(256) void topk_filter_kernel(TopkArgs a) {
-  constexpr int kSub = 4096;  // columns per round: 16 per thread
-  __shared__ uint32_t lh[kHistBins];
-  __shared__ uint32_t sh[16];
-  const int r = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int n = row_valid_len(a, r);
-  const int c0 = blockIdx.x * a.chunk, c1 = min(c0 + a.chunk, n);
-  const float *srow = a.scores + (size_t)r * a.ld;
-  const int32_t *mrow = MAP ? a.map + (size_t)r * a.ld : nullptr;
-  const bool vec = (a.ld % 4) == 0 && ((uintptr_t)a.scores & 15) == 0;  // 16-byte aligned rows
-
-  auto load_round = [&](int sb, float (&sv)[4][4]) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int cf = sb + u * 1024 + 4 * tid;
-      if (vec && cf + 3 < c1) {
-        const float4 x = *(const float4 *)(srow + cf);
-        sv[u][0] = x.x; sv[u][1] = x.y; sv[u][2] = x.z; sv[u][3] = x.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sv[u][e] = cf + e < c1 ? srow[cf + e] : 0.f;
-      }
-    }
-  };
-  // the first round's scores are requested before the threshold is known
-  float sv[4][4];
-  load_round(c0, sv);
-  {
-    const uint4 *h4 = (const uint4 *)(a.hist + (size_t)r * kHistBins);
-#pragma unroll
-    for (int i = 0; i < kHistBins / 4 / 256; ++i) ((uint4 *)lh)[tid + 256 * i] = h4[tid + 256 * i];
-  }
-  __syncthreads();
-  const Thresh th = threshold_from_lds<256>(lh, (uint32_t)a.k, sh);
-  if (blockIdx.x == 0 && tid == 0) {
-    uint32_t *cnt = a.counters + (size_t)r * kRowCounters;
-    cnt[4] = (uint32_t)th.b1;
-    cnt[5] = th.above;
-    cnt[6] = th.eq;
-    cnt[7] = th.kk;
-  }
-  if (th.kk == 0) return;  // uniform; the finish reads nothing else then
-  const bool keep = th.eq <= (uint32_t)a.cap;
-  uint32_t *cnt = a.counters + (size_t)r * kRowCounters;
-  int32_t *irow = a.idx + (size_t)r * a.k;
-  float *vrow = a.val ? a.val + (size_t)r * a.k : nullptr;
-  uint2 *crow = a.cand + (size_t)r * a.cap;
-  const bool solo = gridDim.x == 1;
-  uint32_t run_sel = 0, run_cnd = 0;
-  for (int sb = c0; sb < c1; sb += kSub) {  // uniform trip count
-    if (sb != c0) load_round(sb, sv);
-    // the round's map entries, all issued at once from clamped columns (a
-    // load under a branch would wait for every load before it)
-    int32_t mv[4][4];
-    if constexpr (MAP) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mv[u][e] = mrow[min(sb + u * 1024 + 4 * tid + e, c1 - 1)];
-    }
-    uint32_t fs = 0, fc = 0;  // this thread's 16 columns: above b1 / equal to b1
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = sb + u * 1024 + 4 * tid + e;
-        const bool valid = c < c1 && (!MAP || mv[u][e] >= 0);
-        const int dg = (int)(order_key(sv[u][e]) >> kHistShift);
-        fs |= (valid && dg > th.b1 ? 1u : 0u) << (u * 4 + e);
-        fc |= (valid && keep && dg == th.b1 ? 1u : 0u) << (u * 4 + e);
-      }
-    }
-    const uint32_t mine = ((uint32_t)__popc(fs) << 16) | (uint32_t)__popc(fc);
-    uint32_t total;
-    const uint32_t excl = block_scan<256>(mine, sh, total) - mine;
-    // one global atomic per counter per round reserves this workgroup's range;
-    // a workgroup that owns the whole row keeps its own running offsets
-    if (tid == 0) {
-      if (solo) {
-        sh[8] = run_sel;
-        sh[9] = run_cnd;
-      } else {
-        // counters 0 and 1 as one 64-bit word (low: selected, high:
-        // candidates; a row's counts stay far below 2^32, so no carry
-        // crosses): one atomic, one round trip
-        const unsigned long long o = atomicAdd(
-            (unsigned long long *)cnt, ((unsigned long long)(total & 0xFFFFu) << 32) | (total >> 16));
-        sh[8] = (uint32_t)o;
-        sh[9] = (uint32_t)(o >> 32);
-      }
-    }
-    run_sel += total >> 16;
-    run_cnd += total & 0xFFFFu;
-    __syncthreads();
-    uint32_t so = sh[8] + (excl >> 16), co = sh[9] + (excl & 0xFFFFu);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int bit = u * 4 + e;
-        const int c = sb + u * 1024 + 4 * tid + e;
-        if ((fs >> bit) & 1u) {
-          if (so < th.above) {
-            irow[so] = MAP ? mv[u][e] : c;
-            if (vrow) vrow[so] = sv[u][e];
-          }
-          ++so;
-        }
-        if ((fc >> bit) & 1u) {
-          if (co < (uint32_t)a.cap) crow[co] = make_uint2(order_key(sv[u][e]), (uint32_t)c);
-          ++co;
-        }
-      }
-    }
-    __syncthreads();  // sh[8..9] are rewritten next round
-  }
 }
 
 // Resolve the candidates of the threshold digit: 8-bit digit passes over
@@ -293,65 +164,6 @@ __device__ __forceinline__ void resolve_candidates(
     }
     __syncthreads();
   }
-}
-
-// ------------------------------------------------------------------- finish
-template <bool MAP>
-__global__ __launch_bounds__(kSelThreads) void topk_finish_kernel(TopkArgs a) {
-  constexpr int NT = kSelThreads;
-  constexpr int NW = NT / kWave;
-  __shared__ uint64_t cs[kSelCap];
-  __shared__ uint64_t cs2[kSelCompact];
-  __shared__ uint32_t hs[256];
-  __shared__ uint32_t sh[NW + 16];  // [0, NW) scan scratch, then counters and pass results
-  uint32_t *ctr = sh + NW;          // [0] next output slot [1] compacted
-  uint32_t *res = sh + NW + 4;      // [0] digit [1] count above it [2] count in it
-  const int r = blockIdx.x;
-  const int tid = threadIdx.x;
-  const uint32_t *cnt = a.counters + (size_t)r * kRowCounters;
-  Thresh th;
-  {
-    const uint4 c4 = *(const uint4 *)(cnt + 4);  // the filter's b1, above, eq, kk in one load
-    th.b1 = (int)c4.x;
-    th.above = c4.y;
-    th.eq = c4.z;
-    th.kk = c4.w;
-  }
-
-  int32_t *irow = a.idx + (size_t)r * a.k;
-  float *vrow = a.val ? a.val + (size_t)r * a.k : nullptr;
-  for (int i = (int)th.kk + tid; i < a.k; i += NT) {
-    irow[i] = -1;
-    if (vrow) vrow[i] = -INFINITY;
-  }
-  if (th.kk == 0) return;  // uniform
-
-  const int n = row_valid_len(a, r);
-  const float *srow = a.scores + (size_t)r * a.ld;
-  const int32_t *mrow = MAP ? a.map + (size_t)r * a.ld : nullptr;
-  const bool keep = th.eq <= (uint32_t)a.cap;
-  const int ncur = keep ? (int)min(th.eq, (uint32_t)a.cap) : 0;
-  if (keep) {  // four candidates per thread in flight (clamped loads, guarded stores)
-    const uint2 *crow = a.cand + (size_t)r * a.cap;
-    for (int i0 = 0; i0 < ncur; i0 += 4 * NT) {
-      uint2 e[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) e[u] = crow[min(i0 + u * NT + tid, ncur - 1)];
-      int32_t tok[4];  // every clamped entry holds a valid column
-#pragma unroll
-      for (int u = 0; u < 4; ++u) tok[u] = MAP ? mrow[e[u].y] : (int)e[u].y;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * NT + tid;
-        if (i < ncur) cs[i] = composite(e[u].x, tok[u]);
-      }
-    }
-  }
-  if (tid == 0) ctr[0] = th.above;
-  __syncthreads();
-
-  resolve_candidates<MAP, NT>(cs, ncur, keep, n, srow, mrow, th, irow, vrow, cs, cs2, hs, sh, ctr, res,
-                              (uint64_t)(uint32_t)th.b1 << 52, 0xFFFull << 52, 44, 0u);
 }
 
 // --------------------------------------------------------------- row select
@@ -568,18 +380,18 @@ __device__ __forceinline__ void sample_finish(const TopkArgs &a, int r, int n, u
 }
 
 template <bool MAP, bool REG>
-__device__ __forceinline__ void rowselect_row(const TopkArgs &a, const int r) {
+__device__ __forceinline__ void rowselect_row(const TopkArgs &a, const int r, SelLds &L) {
   constexpr int NT = kSelThreads;
   constexpr int NW = NT / kWave;
   constexpr int U = kSelU;
   constexpr int RR = REG ? kRegRounds : 1;  // rounds held in registers
-  __shared__ uint64_t cs[kSelCap];
-  __shared__ uint64_t cs2[kSelCompact];
-  __shared__ uint32_t hs[256];
-  __shared__ uint32_t sh[NW + 16];
+  uint64_t *cs = L.cs;
+  uint64_t *cs2 = L.cs2;
+  uint32_t *hs = L.hs;
+  uint32_t *sh = L.sh;
   uint32_t *ctr = sh + NW;       // [0] next output slot [1] compacted
   uint32_t *res = sh + NW + 4;   // [0] digit [1] count above it [2] count in it
-  __shared__ unsigned long long cnt64;  // (above emitted << 32) | candidates collected
+  unsigned long long &cnt64 = L.cnt64;  // (above emitted << 32) | candidates collected
   uint32_t *lh = (uint32_t *)cs;  // pass-1 histogram lives in the candidate array
   const int tid = threadIdx.x;
   const int n = row_valid_len(a, r);
@@ -738,31 +550,11 @@ __device__ __forceinline__ void rowselect_row(const TopkArgs &a, const int r) {
                               44, 0u);
 }
 
-// -------------------------------------------------------------------- fill
-__global__ void fill_u32_kernel(uint32_t *p, size_t n, uint32_t v) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x)
-    p[i] = v;
-}
-
-hipError_t launch_fill_u32(uint32_t *p, size_t n, uint32_t v, hipStream_t st) {
-  if (n == 0) return hipSuccess;
-  const size_t blocks = (n + 255) / 256;
-  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
-                     dim3(256), 0, st, p, n, v);
-  return hipGetLastError();
-}
-
-hipError_t launch_topk_hist(const TopkArgs &a, uint32_t *hist, hipStream_t st) {
-  dim3 grid((a.ld + a.chunk - 1) / a.chunk, a.rows);
-  hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(256), 0, st, a, hist);
-  return hipGetLastError();
-}
-
 // One workgroup per row.
 template <bool MAP, bool REG>
 __global__ __launch_bounds__(kSelThreads) void topk_rowselect_kernel(TopkArgs a) {
-  rowselect_row<MAP, REG>(a, blockIdx.x);
+  __shared__ SelLds L;
+  rowselect_row<MAP, REG>(a, blockIdx.x, L);
 }
 
 // The rows the streamed select left (counter 7 set): a grid of at most 256
@@ -774,6 +566,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_flagged_kernel(TopkArgs a) {
   // this workgroup's rows r = blockIdx.x + i * gridDim.x, their flags read
   // 1024 at a time in one round of loads
   __shared__ uint32_t fl[kSelThreads];
+  __shared__ SelLds L;
   for (int i0 = 0; blockIdx.x + i0 * gridDim.x < a.rows; i0 += kSelThreads) {
     {
       const int r = blockIdx.x + (i0 + threadIdx.x) * gridDim.x;
@@ -784,11 +577,251 @@ __global__ __launch_bounds__(kSelThreads) void topk_flagged_kernel(TopkArgs a) {
       const int r = blockIdx.x + (i0 + i) * gridDim.x;
       if (r >= a.rows) break;
       if (fl[i] == 0u) continue;  // uniform
-      rowselect_row<false, false>(a, r);
+      rowselect_row<false, false>(a, r, L);
       __syncthreads();  // the next row reuses the LDS
     }
     __syncthreads();
   }
+}
+
+// ------------------------------------------------------------------ merge
+// The crossing bin of a 256-bin LDS histogram hs counted from the top: the
+// bin where the count reaches `need`, and the count above it, to res[0..1]
+// (res[2] = the bin's own count).  Uniform control flow (barriers).
+template <int NT>
+__device__ __forceinline__ void crossing256(const uint32_t *hs, uint32_t need, uint32_t *sh, uint32_t *res) {
+  const int tid = threadIdx.x;
+  const uint32_t v = tid < 256 ? hs[255 - tid] : 0u;  // thread 0: the largest digit
+  uint32_t total;
+  const uint32_t incl = block_scan<NT>(v, sh, total);
+  if (tid < 256 && incl - v < need && need <= incl) {
+    res[0] = 255u - (uint32_t)tid;
+    res[1] = incl - v;
+    res[2] = v;
+  }
+  __syncthreads();
+}
+
+// One workgroup per row: the exact top-k of the union of the row's chunk
+// lists, or the row select over its scores when the union cannot prove it.
+//  1. headers and the first entries of every list in one round of loads
+//     (a list's slot is at least 256 entries: the first min(512, slot)
+//     entries are loaded before its length is known);
+//  2. the entries as composite keys into LDS, with a 4096-bin histogram of
+//     their top 12 bits: the digit of the kk-th key and the exactness check;
+//  3. the kk-th largest composite key K by 8-bit digit passes over the keys
+//     that match it so far (histograms only, no stores);
+//  4. one pass writes every key >= K (exactly kk of them), positions from a
+//     block scan.
+template <bool MAP>
+__global__ __launch_bounds__(kSelThreads) void topk_merge_kernel(TopkArgs a) {
+  constexpr int NT = kSelThreads, NW = NT / kWave;
+  constexpr int SPEC = 8;  // entries per lane loaded ahead, per list
+  constexpr int PER = kSelCap / NT;
+  __shared__ SelLds L;
+  __shared__ uint32_t off[kMaxLists], cnt[kMaxLists];
+  __shared__ uint32_t maxcut;
+  uint32_t *sh = L.sh;
+  uint32_t *res = sh + NW + 4;
+  uint32_t *lh = (uint32_t *)L.cs2;  // the union's 4096-bin histogram (16 KiB)
+  const int r = blockIdx.x, tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nl = a.nwg;
+  const uint2 *hd = a.lhead + (size_t)r * nl;
+  const uint2 *lrow = a.lists + (size_t)r * nl * a.lcap;
+  const uint32_t spec = (uint32_t)min(SPEC * kWave, a.lcap);
+
+  // 1. headers (thread = list) and, per wave, lists wave and wave + NW
+  const uint2 h = tid < nl ? hd[tid] : make_uint2(0u, 0u);
+  const uint2 *la = lrow + (size_t)min(wave, nl - 1) * a.lcap;
+  const uint2 *lb = lrow + (size_t)min(wave + NW, nl - 1) * a.lcap;
+  uint2 ea[SPEC], eb[SPEC];
+#pragma unroll
+  for (int u = 0; u < SPEC; ++u) {
+    const uint32_t j = min((uint32_t)(lane + kWave * u), spec - 1u);
+    ea[u] = la[j];
+    eb[u] = lb[j];
+  }
+  for (int i = tid; i < kHistBins; i += NT) lh[i] = 0;
+  if (tid == 0) maxcut = 0;
+  uint32_t total;
+  const uint32_t incl = block_scan<NT>(h.x, sh, total);
+  if (tid < nl) {
+    off[tid] = incl - h.x;
+    cnt[tid] = h.x;
+  }
+  const uint32_t mc = wave_max_u32(h.y);
+  if (lane == 0 && mc) atomicMax(&maxcut, mc);
+  __syncthreads();
+  total = __builtin_amdgcn_readfirstlane(total);
+  const uint32_t cut = __builtin_amdgcn_readfirstlane(maxcut);
+  const uint32_t kk = min((uint32_t)a.k, total);
+
+  bool exact = false;
+  int d1 = 0;
+  uint32_t above1 = 0, in1 = 0;
+  if (total <= (uint32_t)kSelCap) {  // uniform
+    // 2. the entries into LDS (list w at off[w]) and their histogram
+    auto place = [&](int w, const uint2 &e, uint32_t j) {
+      if (j < cnt[w]) {
+        L.cs[off[w] + j] = composite(e.x, (int)e.y);
+        atomicAdd(&lh[e.x >> kHistShift], 1u);
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < SPEC; ++u) {
+      const uint32_t j = (uint32_t)(lane + kWave * u);
+      if (wave < nl) place(wave, ea[u], j);
+      if (wave + NW < nl) place(wave + NW, eb[u], j);
+    }
+    // the rest: entries past the first `spec` of these lists, and whole
+    // lists past the first 2 NW
+    for (int w = wave; w < nl; w += NW) {
+      const uint32_t c = cnt[w];
+      const uint2 *lw = lrow + (size_t)w * a.lcap;
+      for (uint32_t j0 = w < 2 * NW ? spec : 0u; j0 < c; j0 += SPEC * kWave) {
+        uint2 e[SPEC];
+#pragma unroll
+        for (int u = 0; u < SPEC; ++u) e[u] = lw[min(j0 + lane + kWave * u, c - 1u)];
+#pragma unroll
+        for (int u = 0; u < SPEC; ++u) place(w, e[u], j0 + lane + kWave * u);
+      }
+    }
+    __syncthreads();
+    const Thresh th = threshold_from_lds<NT>(lh, kk, sh);
+    d1 = __builtin_amdgcn_readfirstlane(th.b1);
+    above1 = __builtin_amdgcn_readfirstlane(th.above);
+    in1 = __builtin_amdgcn_readfirstlane(th.eq);
+    // the union's top-k is the row's when no chunk dropped anything, or when
+    // it holds k keys and the k-th key's digit is at least every cutoff
+    exact = cut == 0u || (kk == (uint32_t)a.k && (uint32_t)d1 >= cut);
+  }
+  if (!exact) {  // uniform: the exact select over the whole score row
+    __syncthreads();
+    rowselect_row<MAP, false>(a, r, L);
+    return;
+  }
+  int32_t *irow = a.idx + (size_t)r * a.k;
+  float *vrow = a.val ? a.val + (size_t)r * a.k : nullptr;
+  // 3. the kk-th largest composite key: keys whose bits above `shift` exceed
+  // (prefix >> shift) are in; the digit passes narrow the prefix until the
+  // crossing digit holds exactly the keys still needed
+  uint64_t prefix = 0, mask = 0;
+  int shift = 64;
+  if (kk > 0) {
+    uint32_t need = kk - above1;
+    prefix = (uint64_t)(uint32_t)d1 << 52;
+    mask = 0xFFFull << 52;
+    shift = 52;
+    uint32_t incnt = in1;
+    uint32_t *hs = L.hs;
+    while (incnt != need && shift > 0) {  // uniform; the keys are unique, so it ends by shift 0
+      shift = max(shift - 8, 0);
+      if (tid < 256) hs[tid] = 0;
+      __syncthreads();
+      for (uint32_t i = tid; i < total; i += NT) {
+        const uint64_t ck = L.cs[i];
+        if ((ck & mask) == prefix) atomicAdd(&hs[(uint32_t)(ck >> shift) & 0xFFu], 1u);
+      }
+      __syncthreads();
+      crossing256<NT>(hs, need, sh, res);
+      const uint32_t d = __builtin_amdgcn_readfirstlane(res[0]);
+      need -= __builtin_amdgcn_readfirstlane(res[1]);
+      incnt = __builtin_amdgcn_readfirstlane(res[2]);
+      prefix |= (uint64_t)d << shift;
+      mask |= 0xFFull << shift;
+      __syncthreads();
+    }
+  }
+  // 4. every key whose bits from `shift` up are >= those of the prefix
+  const uint64_t lim = shift >= 64 ? ~0ull : prefix >> shift;
+  uint32_t mine = 0;
+  uint32_t selbits = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const uint32_t i = (uint32_t)(tid + NT * u);
+    if (i < total && shift < 64 && (L.cs[i] >> shift) >= lim) selbits |= 1u << u;
+  }
+  mine = (uint32_t)__popc(selbits);
+  uint32_t tot;
+  uint32_t pos = block_scan<NT>(mine, sh, tot) - mine;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    if ((selbits >> u) & 1u) {
+      const uint64_t ck = L.cs[tid + NT * u];
+      if (pos < kk) {
+        irow[pos] = (int32_t)(~(uint32_t)ck);
+        if (vrow) vrow[pos] = key_to_float((uint32_t)(ck >> 32));
+      }
+      ++pos;
+    }
+  }
+  for (int i = (int)kk + tid; i < a.k; i += NT) {
+    irow[i] = -1;
+    if (vrow) vrow[i] = -INFINITY;
+  }
+}
+
+// Chunk lists of caller-provided score rows (misa_topk with few long rows):
+// one 256-thread workgroup per (chunk of kListChunk columns, row).
+template <bool MAP>
+__global__ __launch_bounds__(256) void topk_lists_kernel(TopkArgs a) {
+  constexpr int NT = 256, PER = kListChunk / NT;
+  __shared__ float sc[kListChunk];
+  __shared__ uint32_t lh[kHistBins];
+  __shared__ int32_t tk[MAP ? kListChunk : 1];
+  __shared__ uint32_t sh[NT / kWave + 8];
+  const int r = blockIdx.y, tid = threadIdx.x;
+  const int n_row = row_valid_len(a, r);
+  const int c0 = blockIdx.x * kListChunk, c1 = min(c0 + kListChunk, n_row);
+  const float *srow = a.scores + (size_t)r * a.ld;
+  const int32_t *mrow = MAP ? a.map + (size_t)r * a.ld : nullptr;
+  for (int b = tid; b < kHistBins; b += NT) lh[b] = 0;
+  __syncthreads();
+  uint32_t nv = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int i = tid + NT * u, c = c0 + i;
+    const float x = c < c1 ? srow[c] : -INFINITY;
+    const int32_t t = MAP ? (c < c1 ? mrow[c] : -1) : c;
+    const bool ok = c < c1 && (!MAP || t >= 0);
+    sc[i] = x;
+    if (MAP) tk[i] = t;
+    if (ok) {
+      atomicAdd(&lh[order_key(x) >> kHistShift], 1u);
+      ++nv;
+    }
+  }
+  uint32_t nvalid;
+  block_scan<NT>(nv, sh, nvalid);  // (its barriers also publish sc, tk and lh)
+  nvalid = __builtin_amdgcn_readfirstlane(nvalid);
+  const int n = max(0, c1 - c0);
+  const uint32_t quota = chunk_quota(a.k, (int)nvalid, n_row);
+  const uint32_t cap = min((uint32_t)a.lcap, 2u * quota + 64u);
+  chunk_list<NT, PER>(sc, n, lh, nvalid, quota, cap,
+                      [&](int i) { return !MAP || tk[i] >= 0; },
+                      [&](int i) { return MAP ? tk[i] : c0 + i; },
+                      a.lists + ((size_t)r * a.nwg + blockIdx.x) * a.lcap,
+                      a.lhead + (size_t)r * a.nwg + blockIdx.x, sh);
+}
+
+hipError_t launch_topk_merge(const TopkArgs &a, hipStream_t st) {
+  if (a.nwg < 1 || a.nwg > kMaxLists) return hipErrorInvalidValue;
+  if (a.map)
+    hipLaunchKernelGGL(topk_merge_kernel<true>, dim3(a.rows), dim3(kSelThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(topk_merge_kernel<false>, dim3(a.rows), dim3(kSelThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_lists(const TopkArgs &a, hipStream_t st) {
+  if (a.nwg != (a.ld + kListChunk - 1) / kListChunk || a.lcap < kListChunk) return hipErrorInvalidValue;
+  const dim3 grid(a.nwg, a.rows);
+  if (a.map)
+    hipLaunchKernelGGL(topk_lists_kernel<true>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(topk_lists_kernel<false>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------ streamed select
@@ -1124,22 +1157,6 @@ hipError_t launch_topk_rowselect(const TopkArgs &a, hipStream_t st) {
     else
       hipLaunchKernelGGL((topk_rowselect_kernel<false, false>), grid, dim3(kSelThreads), 0, st, a);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_topk_select(const TopkArgs &a, hipStream_t st) {
-  if (a.cap > kSelCap) return hipErrorInvalidValue;
-  dim3 grid((a.ld + a.chunk - 1) / a.chunk, a.rows);
-  if (a.map)
-    hipLaunchKernelGGL(topk_filter_kernel<true>, grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(topk_filter_kernel<false>, grid, dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.map)
-    hipLaunchKernelGGL(topk_finish_kernel<true>, dim3(a.rows), dim3(kSelThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(topk_finish_kernel<false>, dim3(a.rows), dim3(kSelThreads), 0, st, a);
   return hipGetLastError();
 }
 

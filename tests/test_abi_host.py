@@ -129,7 +129,8 @@ def test_validation_before_any_hip_call(lib):
     assert lib.misa_score_topk(ctypes.byref(b), F, 8, 64, F, None, F, small, None) == ERR_WORKSPACE
     assert lib.indexer_dense(ctypes.byref(b), 64, F, None, F, small, None) == ERR_WORKSPACE
     assert lib.misa_rerank(ctypes.byref(b), F, 128, 64, F, None, F, small, None) == ERR_WORKSPACE
-    assert lib.misa_topk(F, 4, 64, F, 8, F, None, F, small, None) == ERR_WORKSPACE
+    tiny = ctypes.c_size_t(16)
+    assert lib.misa_topk(F, 4, 64, F, 8, F, None, F, tiny, None) == ERR_WORKSPACE
     assert lib.misa_indexer(ctypes.byref(b), F, 64, 8, 0, 64, F, None, F, None, F, small, None) == ERR_WORKSPACE
     assert lib.misa_indexer(ctypes.byref(b), None, 64, 8, 0, 64, F, None, F, None, F, big, None) == ERR_NULL
     assert lib.misa_indexer(ctypes.byref(b), F, 64, 9999, 0, 64, F, None, F, None, F, big, None) == ERR_SHAPE
@@ -148,6 +149,13 @@ def test_validation_before_any_hip_call(lib):
     assert lib.hisa_indexer(ctypes.byref(b), F, 64, 4, None, 0, 8, F, None, F, small, None) == ERR_WORKSPACE
     assert lib.hisa_blocks(ctypes.byref(b), F, 64, 4, None, 0, F, F, F, small, None) == ERR_WORKSPACE
     assert lib.hisa_blocks(ctypes.byref(b), F, 64, 4, None, 0, F, F, None, big, None) == ERR_NULL
+    # the streaming-read probe: (buf, bytes, wgs, sink, stream, ev0, ev1)
+    assert lib.misa_stream_read(None, 1024, 4, F, None, None, None) == ERR_NULL
+    assert lib.misa_stream_read(F, 1024, 4, None, None, None, None) == ERR_NULL
+    assert lib.misa_stream_read(P(FAKE + 4), 1024, 4, F, None, None, None) == ERR_UNSUPPORTED
+    assert lib.misa_stream_read(F, 1000, 4, F, None, None, None) == ERR_UNSUPPORTED
+    assert lib.misa_stream_read(F, 1024, 0, F, None, None, None) == ERR_SHAPE
+    assert lib.misa_stream_read(F, 0, 4, F, None, None, None) == ERR_SHAPE
     # the allocation-free indexer: (b, pooled, B, h, mode, k, heads, head_score, idx, val,
     # stream); every check, the scratch limit included, comes before any HIP call
     assert lib.misa_indexer_noalloc(ctypes.byref(b), None, 64, 8, 0, 64, F, None, F, None, None) == ERR_NULL
@@ -174,4 +182,4 @@ def test_validation_before_any_hip_call(lib):
     assert lib.hisa_indexer(ctypes.byref(b), U, 64, 4, None, 0, 8, F, None, F, big, None) == ERR_UNSUPPORTED
     assert lib.hisa_blocks(ctypes.byref(b), F, 64, 4, None, 0, F, F, U, big, None) == ERR_UNSUPPORTED
     # score rows given to misa_topk may start anywhere a float may
-    assert lib.misa_topk(U, 4, 64, F, 8, F, None, F, small, None) == ERR_WORKSPACE
+    assert lib.misa_topk(U, 4, 64, F, 8, F, None, F, ctypes.c_size_t(16), None) == ERR_WORKSPACE

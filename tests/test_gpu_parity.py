@@ -307,6 +307,46 @@ def test_score_topk(S, Lmax, T, H, seed, k):
     assert np.array_equal(np.sort(di, 1), np.sort(np_(dref), 1))
 
 
+@pytest.mark.parametrize("concentrated", [False, True])
+def test_two_stage_select_on_scored_rows(concentrated):
+    """Few long rows take the two-stage select: each scoring workgroup keeps
+    its chunk's share of the row's top-k, and the merge takes the top-k of
+    the union.  With the top-k spread over the row the union proves the
+    result; with most of it packed into a few chunks (keys aligned with a
+    positive-weight head along one stretch of the sequence) those chunks
+    drop entries of the true top-k, the merge detects it and selects from
+    the whole score row.  Both are checked exactly against the kernel's own
+    scores and against the oracle's selection."""
+    abi = _abi()
+    S, Lmax, T, H, k = 3, 40000, 5, 16, 2048
+    q_seq = np.array([0, 1, 2, 0, 1], np.int32)
+    q_pos = np.array([Lmax - 1, 39000, 17000, 25000, Lmax - 1], np.int32)
+    case = synth.random_case(S, Lmax, T, H, seed=41, q_pos=q_pos, q_seq=q_seq)
+    if concentrated:
+        keys = synth.bf16_bits_to_f32(case["keys"]).copy()
+        for t in range(T):
+            j = int(np.argmax(case["w"][t]))
+            qd = synth.bf16_bits_to_f32(case["q"][t, j])
+            lo = 3000 + 1000 * t
+            keys[q_seq[t], lo:lo + 2500] += 0.5 * qd / np.linalg.norm(qd)
+        case["keys"] = synth.to_bf16_bits(keys)
+    b = upload(case)
+    ob = orc.Batch.from_case(case)
+    rng = np.random.default_rng(3)
+    heads = np.stack([rng.permutation(H)[:4] for _ in range(T)]).astype(np.int32)
+    for hh in (None, heads):
+        th = None if hh is None else torch.from_numpy(hh).cuda()
+        idx, val = abi.score_topk(b, th, k)
+        idx, val = np_(idx), np_(val)
+        rows = np_(abi.score(b, th))
+        osc = orc.scores(ob, hh)
+        for t in range(T):
+            n = int(q_pos[t]) + 1
+            parity.check_exact_topk(idx[t], val[t], rows[t], n, k, orc.topk_f32)
+            oi = orc.topk(osc[t, :n], k)[0]
+            parity.check_set(idx[t], oi, lambda i: osc[t, i], n, k, parity.row_sbar(osc[t], n))
+
+
 # ------------------------------------------------------- pooled-cache append
 @pytest.mark.parametrize("B", [1, 16, 64, 128])
 def test_pool_append_matches_fresh_pool(B):
