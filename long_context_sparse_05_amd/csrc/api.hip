@@ -87,7 +87,7 @@ SelectLayout select_layout(size_t rows, size_t ld, int k, bool with_scores) {
   L.counters = off;
   off = align_up(off + rows * kRowCounters * sizeof(uint32_t));
   L.lhead = off;
-  if (L.lists_on) off = align_up(off + rows * (size_t)kMaxLists * sizeof(uint2));
+  if (L.lists_on) off = align_up(off + rows * (size_t)kMaxLists * sizeof(uint4));
   L.lists = off;
   if (L.lists_on) off = align_up(off + rows * (ld + (size_t)kListChunk) * sizeof(uint2));
   L.total = off;
@@ -192,7 +192,7 @@ int run_select(const ScoreArgs *score, const float *scores_in, int rows, int ld,
   t.k = k;
   if (L.lists_on) {
     t.lists = (uint2 *)((char *)ws + L.lists);
-    t.lhead = (uint2 *)((char *)ws + L.lhead);
+    t.lhead = (uint4 *)((char *)ws + L.lhead);
     t.lcap = score ? score->chunk : kListChunk;
     t.nwg = (ld + t.lcap - 1) / t.lcap;
   }

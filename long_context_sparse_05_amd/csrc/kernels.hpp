@@ -28,7 +28,7 @@ struct ScoreArgs {
   // workgroup x of row t writes list [t][x][lcap] and its header [t][x]
   // (entries, cutoff digit), keeping its share of the row's top k.
   uint2 *lists;
-  uint2 *lhead;
+  uint4 *lhead;
   int lcap, k;
   // The router's partial sums [T][nparts][H] (route_partial_kernel), or
   // nullptr: the prologue then reduces and ranks them (route_finish.hpp)
@@ -77,7 +77,7 @@ struct TopkArgs {
   // the rows' chunk candidate lists [rows][nwg][lcap] and headers [rows][nwg]
   // (two-stage top-k of few long rows: topk_merge_kernel)
   uint2 *lists;
-  uint2 *lhead;
+  uint4 *lhead;
   int nwg, lcap;
   int32_t *idx;            // [rows][k]
   float *val;              // [rows][k] or nullptr

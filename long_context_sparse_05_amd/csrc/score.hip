@@ -54,7 +54,7 @@ __global__ __launch_bounds__(NW * 64) void score_rows_kernel(ScoreArgs a) {
   __shared__ uint4 tile[NW][16 * kKeyRowLds / 16];
   __shared__ int32_t ctok[GATHER ? kMaxScoreChunk : 1];  // the chunk's candidate tokens
   __shared__ float csc[kMaxScoreChunk];                   // the chunk's scores
-  __shared__ uint32_t lsh[16];                            // scan scratch, valid-entry count
+  __shared__ uint32_t lsh[2 * NW + 9];                    // scan scratch; [2 NW + 8] valid-entry count
   const int t = blockIdx.y;
   const int lane = lane_id();
   // wave-uniform, and known to be: the step loop below branches on scalars
@@ -72,12 +72,12 @@ __global__ __launch_bounds__(NW * 64) void score_rows_kernel(ScoreArgs a) {
 
   if (lists) {
     for (int b = threadIdx.x; b < kHistBins; b += NT) lds_hist[b] = 0;
-    if (threadIdx.x == 0) lsh[15] = 0;
+    if (threadIdx.x == 0) lsh[2 * NW + 8] = 0;
     if (GATHER) __syncthreads();  // the count is zero before the candidate loop adds to it
   }
   if (!GATHER && c0 >= nvalid) {  // uniform across the workgroup: no barrier follows
     for (int c = c0 + threadIdx.x; c < c1; c += NT) srow[c] = -INFINITY;
-    if (lists && threadIdx.x == 0) a.lhead[(size_t)t * gridDim.x + blockIdx.x] = make_uint2(0u, 0u);
+    if (lists && threadIdx.x == 0) a.lhead[(size_t)t * gridDim.x + blockIdx.x] = make_uint4(0u, 0u, 0u, 0u);
     return;
   }
 
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(NW * 64) void score_rows_kernel(ScoreArgs a) {
         orow[c] = v;
         nv += v >= 0 ? 1u : 0u;
       }
-      if (lists && nv) atomicAdd(&lsh[15], nv);
+      if (lists && nv) atomicAdd(&lsh[2 * NW + 8], nv);
     } else {
       const int32_t *crow = a.cand + (size_t)t * a.ncols;
       uint32_t nv = 0;
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(NW * 64) void score_rows_kernel(ScoreArgs a) {
         ctok[c - c0] = v;
         nv += v >= 0 ? 1u : 0u;
       }
-      if (lists && nv) atomicAdd(&lsh[15], nv);
+      if (lists && nv) atomicAdd(&lsh[2 * NW + 8], nv);
     }
   }
   if (lists || GATHER) __syncthreads();
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(NW * 64) void score_rows_kernel(ScoreArgs a) {
   __syncthreads();
   if (lists) {  // the chunk's share of the row's top k, for the merge (before the
     // score stores: work after them would wait for the stores to land)
-    const uint32_t nvc = GATHER ? lsh[15] : (uint32_t)max(0, min(c1, nvalid) - c0);
+    const uint32_t nvc = GATHER ? lsh[2 * NW + 8] : (uint32_t)max(0, min(c1, nvalid) - c0);
     const uint32_t quota = chunk_quota(a.k, (int)nvc, nvalid);
     const uint32_t cap = min((uint32_t)a.lcap, 2u * quota + 64u);
     const size_t slot = (size_t)t * gridDim.x + blockIdx.x;

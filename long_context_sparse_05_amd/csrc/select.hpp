@@ -112,16 +112,17 @@ __device__ __forceinline__ uint32_t chunk_quota(int k, int n, int n_row) {
   return q >= (float)n ? (uint32_t)n : (uint32_t)q;
 }
 
-// List entry: (order key, token id); header: (entries, cutoff digit).
+// List entry: (order key, token id); header: (entries, cutoff digit,
+// largest key in the list, 0).
 // sc: the chunk's n scores in LDS; lh: the 4096-bin histogram of the top 12
 // key bits of its nvalid valid entries (LDS); valid(i) / tok(i): entry i's
 // validity and token id.  Every thread of the NT-thread workgroup calls this
-// with uniform arguments (it contains barriers).  At most cap entries are
-// written to out.
+// with uniform arguments (it contains barriers); sh needs 2 NT/64 + 8 words.
+// At most cap entries are written to out.
 template <int NT, int MAXPER, typename Valid, typename Tok>
 __device__ __forceinline__ void chunk_list(const float *sc, int n, const uint32_t *lh, uint32_t nvalid,
                                            uint32_t quota, uint32_t cap, Valid valid, Tok tok, uint2 *out,
-                                           uint2 *head, uint32_t *sh) {
+                                           uint4 *head, uint32_t *sh) {
   const int tid = threadIdx.x;
   uint32_t cut = 0;  // keep every valid entry
   if (quota < nvalid) {
@@ -130,12 +131,18 @@ __device__ __forceinline__ void chunk_list(const float *sc, int n, const uint32_
     // that digit's entries would overflow the list
     cut = th.above + th.eq <= cap ? (uint32_t)th.b1 : (uint32_t)th.b1 + 1u;
   }
-  uint32_t hits = 0;
+  uint32_t hits = 0, kmax = 0;
 #pragma unroll
   for (int u = 0; u < MAXPER; ++u) {
     const int i = tid + NT * u;
-    if (i < n && valid(i) && (order_key(sc[i]) >> kHistShift) >= cut) hits |= 1u << u;
+    const uint32_t key = order_key(sc[min(i, max(n - 1, 0))]);
+    if (i < n && valid(i) && (key >> kHistShift) >= cut) {
+      hits |= 1u << u;
+      kmax = max(kmax, key);
+    }
   }
+  kmax = wave_max_u32(kmax);
+  if (lane_id() == 0) sh[NT / kWave + 7 + threadIdx.x / kWave] = kmax;
   uint32_t total;
   uint32_t pos = block_scan<NT>((uint32_t)__popc(hits), sh, total) - (uint32_t)__popc(hits);
 #pragma unroll
@@ -146,7 +153,11 @@ __device__ __forceinline__ void chunk_list(const float *sc, int n, const uint32_
       ++pos;
     }
   }
-  if (tid == 0) *head = make_uint2(min(total, cap), total <= cap ? cut : 0xFFFFFFFFu);
+  if (tid == 0) {
+    uint32_t m = 0;
+    for (int w = 0; w < NT / kWave; ++w) m = max(m, sh[NT / kWave + 7 + w]);
+    *head = make_uint4(min(total, cap), total <= cap ? cut : 0xFFFFFFFFu, m, 0u);
+  }
 }
 
 }  // namespace misa

@@ -585,54 +585,45 @@ __global__ __launch_bounds__(kSelThreads) void topk_flagged_kernel(TopkArgs a) {
 }
 
 // ------------------------------------------------------------------ merge
-// The crossing bin of a 256-bin LDS histogram hs counted from the top: the
-// bin where the count reaches `need`, and the count above it, to res[0..1]
-// (res[2] = the bin's own count).  Uniform control flow (barriers).
-template <int NT>
-__device__ __forceinline__ void crossing256(const uint32_t *hs, uint32_t need, uint32_t *sh, uint32_t *res) {
-  const int tid = threadIdx.x;
-  const uint32_t v = tid < 256 ? hs[255 - tid] : 0u;  // thread 0: the largest digit
-  uint32_t total;
-  const uint32_t incl = block_scan<NT>(v, sh, total);
-  if (tid < 256 && incl - v < need && need <= incl) {
-    res[0] = 255u - (uint32_t)tid;
-    res[1] = incl - v;
-    res[2] = v;
-  }
-  __syncthreads();
-}
-
 // One workgroup per row: the exact top-k of the union of the row's chunk
 // lists, or the row select over its scores when the union cannot prove it.
 //  1. headers and the first entries of every list in one round of loads
-//     (a list's slot is at least 256 entries: the first min(512, slot)
-//     entries are loaded before its length is known);
-//  2. the entries as composite keys into LDS, with a 4096-bin histogram of
-//     their top 12 bits: the digit of the kk-th key and the exactness check;
-//  3. the kk-th largest composite key K by 8-bit digit passes over the keys
-//     that match it so far (histograms only, no stores);
-//  4. one pass writes every key >= K (exactly kk of them), positions from a
-//     block scan.
+//     (a list's slot holds at least 256 entries: the first min(512, slot)
+//     are loaded before its length is known);
+//  2. the entries as composite keys into LDS, with a histogram of 4096
+//     bins over the union's own key range [lo, hi] -- lo the lowest cutoff,
+//     hi the largest key, both from the headers -- so bins are fine where
+//     the k-th key lies;
+//  3. the bin holding the kk-th key; when it holds more keys than are still
+//     needed they are ranked among themselves (each against all, few keys),
+//     giving the kk-th composite key K (a bin of more than 1024 keys -- heavy
+//     ties -- takes the row select);
+//  4. the exactness check (K's digit against every cutoff), then one pass
+//     writes every key >= K, positions from a block scan.
 template <bool MAP>
 __global__ __launch_bounds__(kSelThreads) void topk_merge_kernel(TopkArgs a) {
   constexpr int NT = kSelThreads, NW = NT / kWave;
   constexpr int SPEC = 8;  // entries per lane loaded ahead, per list
   constexpr int PER = kSelCap / NT;
+  constexpr int NB = kHistBins;  // bins over the union's key range
   __shared__ SelLds L;
   __shared__ uint32_t off[kMaxLists], cnt[kMaxLists];
-  __shared__ uint32_t maxcut;
+  // [0] largest cutoff [1] lowest key bound [2] largest key [3] keys of the
+  // crossing bin; later [0..1] hold the kk-th composite key
+  __shared__ alignas(8) uint32_t red[4];
   uint32_t *sh = L.sh;
-  uint32_t *res = sh + NW + 4;
-  uint32_t *lh = (uint32_t *)L.cs2;  // the union's 4096-bin histogram (16 KiB)
+  uint32_t *lh = (uint32_t *)L.cs2;  // the union's histogram (16 KiB)
   const int r = blockIdx.x, tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = a.nwg;
-  const uint2 *hd = a.lhead + (size_t)r * nl;
+  const uint4 *hd = a.lhead + (size_t)r * nl;
   const uint2 *lrow = a.lists + (size_t)r * nl * a.lcap;
   const uint32_t spec = (uint32_t)min(SPEC * kWave, a.lcap);
+  int32_t *irow = a.idx + (size_t)r * a.k;
+  float *vrow = a.val ? a.val + (size_t)r * a.k : nullptr;
 
   // 1. headers (thread = list) and, per wave, lists wave and wave + NW
-  const uint2 h = tid < nl ? hd[tid] : make_uint2(0u, 0u);
+  const uint4 h = tid < nl ? hd[tid] : make_uint4(0u, 0u, 0u, 0u);
   const uint2 *la = lrow + (size_t)min(wave, nl - 1) * a.lcap;
   const uint2 *lb = lrow + (size_t)min(wave + NW, nl - 1) * a.lcap;
   uint2 ea[SPEC], eb[SPEC];
@@ -642,30 +633,46 @@ __global__ __launch_bounds__(kSelThreads) void topk_merge_kernel(TopkArgs a) {
     ea[u] = la[j];
     eb[u] = lb[j];
   }
-  for (int i = tid; i < kHistBins; i += NT) lh[i] = 0;
-  if (tid == 0) maxcut = 0;
+  for (int i = tid; i < NB; i += NT) lh[i] = 0;
+  if (tid < 4) red[tid] = tid == 1 ? 0xFFFFFFFFu : 0u;
   uint32_t total;
   const uint32_t incl = block_scan<NT>(h.x, sh, total);
   if (tid < nl) {
     off[tid] = incl - h.x;
     cnt[tid] = h.x;
   }
-  const uint32_t mc = wave_max_u32(h.y);
-  if (lane == 0 && mc) atomicMax(&maxcut, mc);
+  {  // largest cutoff; lowest bound of a list's keys (its cutoff digit, 0 when
+     // it kept everything); largest key
+    const bool on = tid < nl && h.x > 0;
+    const uint32_t mc = wave_max_u32(tid < nl ? h.y : 0u);
+    const uint32_t lo = ~wave_max_u32(on ? ~(h.y >= (uint32_t)kHistBins ? 0u : h.y << kHistShift) : 0u);
+    const uint32_t hi = wave_max_u32(on ? h.z : 0u);
+    if (lane == 0) {
+      if (mc) atomicMax(&red[0], mc);
+      atomicMin(&red[1], lo);
+      if (hi) atomicMax(&red[2], hi);
+    }
+  }
   __syncthreads();
   total = __builtin_amdgcn_readfirstlane(total);
-  const uint32_t cut = __builtin_amdgcn_readfirstlane(maxcut);
+  const uint32_t cut = __builtin_amdgcn_readfirstlane(red[0]);
+  // (readfirstlane returns int: compare as unsigned)
+  const uint32_t khi = (uint32_t)__builtin_amdgcn_readfirstlane(red[2]);
+  const uint32_t klo = min((uint32_t)__builtin_amdgcn_readfirstlane(red[1]), khi);
   const uint32_t kk = min((uint32_t)a.k, total);
+  // bin of a key: (key - klo) >> bs, in [0, NB) for every key of the union
+  // (clamped all the same, so no LDS access can leave the histogram)
+  const int bs = max(0, 32 - (int)__clz(khi - klo) - kHistBits);
+  auto bin_of = [&](uint32_t key) { return min((key - klo) >> bs, (uint32_t)NB - 1u); };
 
-  bool exact = false;
-  int d1 = 0;
-  uint32_t above1 = 0, in1 = 0;
-  if (total <= (uint32_t)kSelCap) {  // uniform
+  bool fits = total <= (uint32_t)kSelCap;
+  uint64_t kth = 0;  // the kk-th largest composite key
+  if (fits && kk > 0) {  // uniform
     // 2. the entries into LDS (list w at off[w]) and their histogram
     auto place = [&](int w, const uint2 &e, uint32_t j) {
       if (j < cnt[w]) {
         L.cs[off[w] + j] = composite(e.x, (int)e.y);
-        atomicAdd(&lh[e.x >> kHistShift], 1u);
+        atomicAdd(&lh[bin_of(e.x)], 1u);
       }
     };
 #pragma unroll
@@ -688,61 +695,53 @@ __global__ __launch_bounds__(kSelThreads) void topk_merge_kernel(TopkArgs a) {
       }
     }
     __syncthreads();
+    // 3. the bin holding the kk-th key, counted from the top
     const Thresh th = threshold_from_lds<NT>(lh, kk, sh);
-    d1 = __builtin_amdgcn_readfirstlane(th.b1);
-    above1 = __builtin_amdgcn_readfirstlane(th.above);
-    in1 = __builtin_amdgcn_readfirstlane(th.eq);
-    // the union's top-k is the row's when no chunk dropped anything, or when
-    // it holds k keys and the k-th key's digit is at least every cutoff
-    exact = cut == 0u || (kk == (uint32_t)a.k && (uint32_t)d1 >= cut);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readfirstlane(th.b1);
+    const uint32_t need = kk - __builtin_amdgcn_readfirstlane(th.above);
+    const uint32_t inb = __builtin_amdgcn_readfirstlane(th.eq);
+    if (inb > (uint32_t)NT) {  // uniform: heavy ties in one bin
+      fits = false;
+    } else {
+      // the bin's keys into the (now free) histogram words, one per thread,
+      // each ranked against all of them: the key of rank need - 1 is K
+      uint64_t *bkeys = (uint64_t *)lh;
+      if (tid == 0) red[3] = 0;
+      __syncthreads();
+      for (uint32_t i0 = 0; i0 < total; i0 += NT) {
+        const uint32_t i = i0 + tid;
+        const uint64_t ck = i < total ? L.cs[i] : 0ull;
+        uint32_t pos;
+        if (lds_append(i < total && bin_of((uint32_t)(ck >> 32)) == b, &red[3], pos) && pos < (uint32_t)NT)
+          bkeys[pos] = ck;
+      }
+      __syncthreads();
+      if ((uint32_t)tid < inb) {
+        const uint64_t mine = bkeys[tid];
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < inb; ++j) rank += bkeys[j] > mine ? 1u : 0u;
+        if (rank == need - 1u) ((uint64_t *)&red[0])[0] = mine;  // red[0..1]: K (cutoff already read)
+      }
+      __syncthreads();
+      kth = ((const uint64_t *)&red[0])[0];
+    }
   }
+  // 4. exact when no chunk dropped anything, or the union holds k keys and
+  // K's digit is at least every cutoff
+  const bool exact = fits && (cut == 0u || (kk == (uint32_t)a.k && (uint32_t)(kth >> 52) >= cut));
   if (!exact) {  // uniform: the exact select over the whole score row
     __syncthreads();
     rowselect_row<MAP, false>(a, r, L);
     return;
   }
-  int32_t *irow = a.idx + (size_t)r * a.k;
-  float *vrow = a.val ? a.val + (size_t)r * a.k : nullptr;
-  // 3. the kk-th largest composite key: keys whose bits above `shift` exceed
-  // (prefix >> shift) are in; the digit passes narrow the prefix until the
-  // crossing digit holds exactly the keys still needed
-  uint64_t prefix = 0, mask = 0;
-  int shift = 64;
-  if (kk > 0) {
-    uint32_t need = kk - above1;
-    prefix = (uint64_t)(uint32_t)d1 << 52;
-    mask = 0xFFFull << 52;
-    shift = 52;
-    uint32_t incnt = in1;
-    uint32_t *hs = L.hs;
-    while (incnt != need && shift > 0) {  // uniform; the keys are unique, so it ends by shift 0
-      shift = max(shift - 8, 0);
-      if (tid < 256) hs[tid] = 0;
-      __syncthreads();
-      for (uint32_t i = tid; i < total; i += NT) {
-        const uint64_t ck = L.cs[i];
-        if ((ck & mask) == prefix) atomicAdd(&hs[(uint32_t)(ck >> shift) & 0xFFu], 1u);
-      }
-      __syncthreads();
-      crossing256<NT>(hs, need, sh, res);
-      const uint32_t d = __builtin_amdgcn_readfirstlane(res[0]);
-      need -= __builtin_amdgcn_readfirstlane(res[1]);
-      incnt = __builtin_amdgcn_readfirstlane(res[2]);
-      prefix |= (uint64_t)d << shift;
-      mask |= 0xFFull << shift;
-      __syncthreads();
-    }
-  }
-  // 4. every key whose bits from `shift` up are >= those of the prefix
-  const uint64_t lim = shift >= 64 ? ~0ull : prefix >> shift;
-  uint32_t mine = 0;
+  // every key >= K: exactly kk of them
   uint32_t selbits = 0;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const uint32_t i = (uint32_t)(tid + NT * u);
-    if (i < total && shift < 64 && (L.cs[i] >> shift) >= lim) selbits |= 1u << u;
+    if (kk > 0 && i < total && L.cs[i] >= kth) selbits |= 1u << u;
   }
-  mine = (uint32_t)__popc(selbits);
+  const uint32_t mine = (uint32_t)__popc(selbits);
   uint32_t tot;
   uint32_t pos = block_scan<NT>(mine, sh, tot) - mine;
 #pragma unroll
@@ -770,7 +769,7 @@ __global__ __launch_bounds__(256) void topk_lists_kernel(TopkArgs a) {
   __shared__ float sc[kListChunk];
   __shared__ uint32_t lh[kHistBins];
   __shared__ int32_t tk[MAP ? kListChunk : 1];
-  __shared__ uint32_t sh[NT / kWave + 8];
+  __shared__ uint32_t sh[2 * NT / kWave + 9];
   const int r = blockIdx.y, tid = threadIdx.x;
   const int n_row = row_valid_len(a, r);
   const int c0 = blockIdx.x * kListChunk, c1 = min(c0 + kListChunk, n_row);

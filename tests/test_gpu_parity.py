@@ -101,6 +101,10 @@ def _topk_rows(rng, rows, ld, kind):
         v = np.full((rows, ld), 0.5, np.float32)
     elif kind == "spread":
         v = (rng.standard_normal((rows, ld)) * np.exp(rng.uniform(-20, 20, (rows, ld)))).astype(np.float32)
+    elif kind == "negative":   # the k-th score is negative (keys below the sign flip)
+        v = (rng.standard_normal((rows, ld)) * 0.05 - 0.2).astype(np.float32)
+    elif kind == "straddle":   # the top k spans zero: positive and negative keys
+        v = (rng.standard_normal((rows, ld)) * 0.05 - 0.1).astype(np.float32)
     else:
         v = rng.standard_normal((rows, ld)).astype(np.float32) * 0.05
     return v
@@ -109,7 +113,7 @@ def _topk_rows(rng, rows, ld, kind):
 @pytest.mark.parametrize("kind,rows,ld,k", [
     ("normal", 6, 5000, 300), ("ties", 5, 3000, 257), ("spread", 4, 70000, 2048),
     ("equal", 2, 20000, 100), ("normal", 3, 100, 100), ("ties", 2, 40000, 1),
-    ("normal", 3, 33000, 16384),
+    ("normal", 3, 33000, 16384), ("negative", 3, 40000, 2048), ("straddle", 4, 131072, 2048),
 ])
 def test_topk_exact(kind, rows, ld, k):
     abi = _abi()
