@@ -1,11 +1,14 @@
 """Benchmark of the MISA indexer decode step on one MI355X.
 
-One step = misa_route + misa_score_topk for every query of the workload
-(decode at 128K context: 16 sequences of 131072 keys, one query each,
-H_I = 64, B = 128, h = 8, k = 2048), inputs resident in HBM.  Block pooling
-runs once per key cache and is timed separately.  Prints one JSON line.
+One step = the fused indexer call (router, routed scoring, top-k) for every
+query of the workload (decode at 128K context: 16 sequences of 131072 keys,
+one query each, H_I = 64, B = 128, h = 8, k = 2048), inputs resident in HBM.
+Block pooling runs once per key cache and is timed separately.  The default
+run also measures the plain streaming-read peak and, as `secondary`, the
+prefill chunk (4096 queries over 65536 keys, MFMA-bound).  Prints one JSON
+line.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-secondary]
 """
 from __future__ import annotations
 
@@ -27,7 +30,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 KEY_BYTES = 128 * 2  # one bf16 indexing key
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "long_context_sparse_05_amd", "csrc", f)
-                  for f in ("score.hip", "common.hpp")]
+                  for f in ("score.hip", "common.hpp", "select.hpp", "route_finish.hpp")]
 
 
 class HipEvents:
@@ -142,10 +145,20 @@ def summarize_counters(workload, fetch_dir, write_dir, cfetch_dir, cwrite_dir):
     return 0
 
 
-def cpu_baseline_rows(case, cfg, rows, reps=3):
-    """The oracle on the query rows `rows` of the workload (all rows unless the
-    workload is too large for the host in ~30 s).  Returns (value, cores,
-    outputs)."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline_rows(case, cfg, rows, reps=3, threads=None):
+    """The oracle on the query rows `rows` of the workload, median of `reps`
+    runs (`threads`: OpenMP threads, default all).  Returns (key-scores/s,
+    threads used, outputs of the last run)."""
     import numpy as np
     from oracle import oracle as orc
     sub = dict(case)
@@ -153,60 +166,77 @@ def cpu_baseline_rows(case, cfg, rows, reps=3):
         sub[key] = np.ascontiguousarray(case[key][rows])
     b = orc.Batch.from_case(sub)
     kind = cfg["kind"]
+    before = orc.num_threads()
+    if threads:
+        orc.set_num_threads(threads)
     times = []
     out = None
-    for _ in range(reps):
-        t0 = time.perf_counter()
-        if kind == "dagger":
-            out = orc.misa_dagger(b, cfg["B"], cfg["h"], cfg["kc"], cfg["k"])
-        elif kind == "hisa":
-            out = orc.hisa(b, cfg["B"], cfg["m"], cfg["k"])
-        elif kind == "misa_hisa":
-            heads, _ = orc.route(b, cfg["B"], cfg["h"])
-            out = orc.hisa(b, cfg["B"], cfg["m"], cfg["k"], heads=heads)
-            out["heads"] = heads
-        elif "h" in cfg:
-            out = orc.misa(b, cfg["B"], cfg["h"], cfg["k"])
-        else:
-            idx, _ = orc.dsa(b, cfg["k"])
-            out = {"idx": idx}
-        times.append(time.perf_counter() - t0)
+    try:
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            if kind == "dagger":
+                out = orc.misa_dagger(b, cfg["B"], cfg["h"], cfg["kc"], cfg["k"])
+            elif kind == "hisa":
+                out = orc.hisa(b, cfg["B"], cfg["m"], cfg["k"])
+            elif kind == "misa_hisa":
+                heads, _ = orc.route(b, cfg["B"], cfg["h"])
+                out = orc.hisa(b, cfg["B"], cfg["m"], cfg["k"], heads=heads)
+                out["heads"] = heads
+            elif "h" in cfg:
+                out = orc.misa(b, cfg["B"], cfg["h"], cfg["k"])
+            else:
+                idx, _ = orc.dsa(b, cfg["k"])
+                out = {"idx": idx}
+            times.append(time.perf_counter() - t0)
+        used = orc.num_threads()
+    finally:
+        orc.set_num_threads(before)
     n = float((sub["q_pos"].astype(np.int64) + 1).sum())
-    return n / float(np.median(times)), orc.num_threads(), out
+    return n / float(np.median(times)), used, out
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="misa_decode_16x128K")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="run only a plain copy of known size (for counter scaling)")
-    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"),
-                    help="rocprofv3 --pmc output dirs of the bench and of --copy-calibration")
-    args = ap.parse_args(argv)
-    if args.summarize_counters:
-        return summarize_counters(args.workload, *args.summarize_counters)
-    if args.copy_calibration:
-        return copy_calibration()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the indexer path here is built and timed on a single "
-              "MI355X; %d GPUs (--gpus %d, WORLD_SIZE %d) is not supported"
-              % (max(args.gpus, world), args.gpus, world), file=sys.stderr)
-        return 2
+READ_PEAK_MIB = 512
 
+
+def measure_read_peak(ev, reps=10):
+    """The plain streaming read (misa_stream_read) of a 512 MiB buffer after a
+    1 GiB fill that evicts the caches, at 512 workgroups (two per CU, as the
+    decode scoring kernel): median and spread of `reps` event-timed runs."""
+    import numpy as np
+    import torch
+    from long_context_sparse_05_amd import abi
+    nbytes = READ_PEAK_MIB << 20
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(3)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    sp = torch.cuda.current_stream().cuda_stream
+    wgs = 512
+    sink = torch.zeros(wgs, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        abi.stream_read(buf, wgs, sink)
+    us = []
+    for i in range(reps):
+        flush.fill_(i & 0xFF)
+        e0, e1 = ev.create(), ev.create()
+        abi.stream_read(buf, wgs, sink, events=(e0, e1))
+        torch.cuda.synchronize()
+        us.append(ev.ms(e0, e1) * 1e3)
+    del buf, flush
+    gbs = [nbytes / u / 1e3 for u in us]
+    return {"GBs_median": float(np.median(gbs)), "GBs_p10_p90": [float(np.percentile(gbs, 10)),
+                                                                 float(np.percentile(gbs, 90))],
+            "bytes": nbytes, "workgroups": wgs, "kernel": "stream_read_kernel (misa_stream_read)",
+            "method": "event-timed, each run after a 1 GiB fill evicting L2 and the MALL"}
+
+
+def measure(workload, K, W, ev, cpu=True, cpu_rows_cap=None):
+    """One workload: warm-up, K back-to-back steps (the headline), the scoring
+    kernel's own duration, separate calls, cold single steps, CPU baseline and
+    a parity summary.  Returns the result fields."""
     import numpy as np
     import torch
     from long_context_sparse_05_amd import abi, synth
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 1
-    abi.load()
-    case, cfg = synth.make_workload(args.workload, seed=0)
+    case, cfg = synth.make_workload(workload, seed=0)
     kind = cfg["kind"]
     routed = "h" in cfg
     hier = kind in ("hisa", "misa_hisa")  # the hierarchical indexer's step
@@ -216,8 +246,6 @@ def main(argv=None):
     b = abi.Batch.from_numpy(case)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
-    ev = HipEvents()
-    K = args.steps
     dev = "cuda"
 
     pool_us = None
@@ -267,7 +295,7 @@ def main(argv=None):
         if kind == "dagger":
             abi.rerank(b, idx, k, idx=fin, val=fin_val, ws=ws_rr)
 
-    for _ in range(args.warmup):
+    for _ in range(W):
         step()
     torch.cuda.synchronize()
     # the timed region: K whole steps, events only at its two ends
@@ -290,7 +318,7 @@ def main(argv=None):
     score_ms = float(np.mean([ev.ms(a, c) for a, c in sev]))
     ms_sep = None
     if routed and not hier:
-        for _ in range(args.warmup):
+        for _ in range(W):
             step_separate()
         ev.record(t_start, sp)
         for _ in range(K):
@@ -310,7 +338,6 @@ def main(argv=None):
         ev.record(cev[i][1], sp)
     torch.cuda.synchronize()
     cold_all = np.array([ev.ms(a, c) for a, c in cev])
-    cold_ms = float(np.mean(cold_all))
     del flush
     step()  # leave the fused call's outputs for the parity check
     torch.cuda.synchronize()
@@ -340,27 +367,16 @@ def main(argv=None):
         alg_bytes = n_keys * KEY_BYTES + b.T * nh * KEY_BYTES  # keys streamed + query rows
         achieved = alg_bytes / (score_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(args.workload),
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(workload),
                 "kernel": "score_rows_kernel (%d-row head tiles, direct rows)" % (16 * ((nh + 15) // 16)),
                 "alg_bytes_per_launch": alg_bytes}
 
     res = {
-        "metric": METRIC,
-        "value": value,
-        "unit": "key-scores/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
         "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": args.workload, "sequences": int(b.S), "context": int(b.Lmax),
+        "value": value,
+        "config": {"workload": workload, "sequences": int(b.S), "context": int(b.Lmax),
                    "queries": int(b.T), "H_I": int(b.H), "B": B, "h": h, "k": k, "d": 128},
         "us_per_batch": ms_step * 1e3,
-        "us_per_batch_cold": cold_ms * 1e3,
         # each cold step bracketed by its own events: median and spread
         "us_per_batch_cold_p10_p50_p90": [float(np.percentile(cold_all, q)) * 1e3 for q in (10, 50, 90)],
         "score_kernel_us": score_ms * 1e3,
@@ -382,7 +398,7 @@ def main(argv=None):
         step_bytes = (n_keys * KEY_BYTES + n_blocks * 128 * 4 + b.T * b.H * (KEY_BYTES + 4)
                       + b.T * k1 * 8 + (b.T * kc * KEY_BYTES if kind == "dagger" else 0))
         res["hbm_frac_whole_step"] = step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS
-    if not args.no_cpu:
+    if cpu:
         if kind == "prefill":  # a bounded sample: 16 query rows spread over the chunk
             rows = np.linspace(0, b.T - 1, 16).astype(np.int64)
             sample = "16 of %d query rows (evenly spaced), median of 3 runs" % b.T
@@ -390,8 +406,12 @@ def main(argv=None):
             rows = np.arange(b.T)
             sample = "all %d queries of the workload, median of 3 runs" % b.T
         cv, cores, out = cpu_baseline_rows(case, cfg, rows)
+        # one thread on a smaller sample: two of the rows
+        r1 = rows[:2]
+        cv1, _, _ = cpu_baseline_rows(case, cfg, r1, reps=1, threads=1)
         res["cpu_baseline"] = {"value": cv, "unit": "key-scores/s", "cores": cores,
-                               "kind": "oracle", "sample": sample}
+                               "kind": "oracle", "sample": sample, "cpu_model": cpu_model(),
+                               "value_1thread": cv1, "sample_1thread": "%d query rows, one run" % len(r1)}
         gi = (fin if kind == "dagger" else idx).cpu().numpy()[rows]
         par = {"rows_checked": int(len(rows)),
                "set_overlap": float(np.mean([len(set(gi[i]) & set(out["idx"][i])) / k
@@ -400,6 +420,76 @@ def main(argv=None):
             gh = heads.cpu().numpy()[rows]
             par["heads_equal"] = bool(np.array_equal(np.sort(gh, 1), np.sort(out["heads"], 1)))
         res["parity_vs_oracle"] = par
+    return res
+
+
+SECONDARY = "misa_prefill_chunk_4096q_L65536"
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="misa_decode_16x128K")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the prefill-chunk record of the default run")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain copy of known size (for counter scaling)")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "CFETCH", "CWRITE"),
+                    help="rocprofv3 --pmc output dirs of the bench and of --copy-calibration")
+    args = ap.parse_args(argv)
+    if args.summarize_counters:
+        return summarize_counters(args.workload, *args.summarize_counters)
+    if args.copy_calibration:
+        return copy_calibration()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the indexer path here is built and timed on a single "
+              "MI355X; %d GPUs (--gpus %d, WORLD_SIZE %d) is not supported"
+              % (max(args.gpus, world), args.gpus, world), file=sys.stderr)
+        return 2
+
+    import torch
+    from long_context_sparse_05_amd import abi
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    abi.load()
+    ev = HipEvents()
+    K, W = args.steps, args.warmup
+    peak = measure_read_peak(ev)
+    r = measure(args.workload, K, W, ev, cpu=not args.no_cpu)
+    roof = r["roofline"]
+    if roof["bound"] == "hbm":
+        roof["measured_read_peak_GBs"] = peak["GBs_median"]
+        roof["frac_of_measured_read_peak"] = roof["achieved"] / peak["GBs_median"]
+    res = {
+        "metric": METRIC,
+        "value": r.pop("value"),
+        "unit": "key-scores/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": r.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+    }
+    res.update(r)
+    res["hbm_read_peak_measured"] = peak
+    if args.workload != SECONDARY and not args.no_secondary:
+        # the prefill chunk (MFMA-bound) beside the decode headline, fewer steps
+        s = measure(SECONDARY, min(K, 10), min(W, 3), ev, cpu=not args.no_cpu)
+        s["us_per_step"] = s.pop("ms_per_step") * 1e3
+        s["key_scores_per_s"] = s.pop("value")
+        for key in ("wall_s_timed", "us_per_batch"):
+            s.pop(key, None)
+        res["secondary"] = s
     print(json.dumps(res), flush=True)
     return 0
 
