@@ -87,6 +87,9 @@ extern "C" {
  *   q_seq    int32 [T]: the sequence of each query row.
  *   q_pos    int32 [T]: the position p_t of each query; its prefix is 0..p_t.
  * d must equal MISA_D; 1 <= H <= MISA_MAX_HEADS; S, T, Lmax >= 1.
+ * Calls that take query rows accept T <= 65535 (rows go on a grid dimension
+ * of that size); misa_pool and misa_pool_append accept S <= 65535, and
+ * misa_topk rows <= 65535.  Larger values return MISA_ERR_UNSUPPORTED.
  */
 typedef struct misa_batch {
   const uint16_t *keys;
@@ -276,8 +279,8 @@ int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B,
  *   Limit: a batch whose MISA_OP_INDEXER workspace (misa_workspace_bytes with
  *   the same B, h, k) exceeds MISA_NOALLOC_SCRATCH_BYTES is rejected with
  *   MISA_ERR_TOO_LARGE before anything is enqueued -- for example 16
- *   sequences of 131072 keys need about 10.5 MiB, 64 such sequences do not
- *   fit.
+ *   sequences of 131072 keys with k = 2048 need about 25 MiB, 32 such
+ *   sequences do not fit.
  *   Every call on one GPU uses the same scratch, and a call leaves its
  *   contents behind: calls on one GPU must be ordered (one stream, or events
  *   between streams); calls that overlap race and give undefined results.
