@@ -1,9 +1,10 @@
 """Parity at the full workload sizes, in the launch configuration the
 benchmark times: the same calls over every query row of each workload
 (16 x 128K decode, 32 x 32K dense, MISA-dagger, the 4096-query prefill
-chunk, HISA and MISA composed with HISA), then the oracle on a few sampled
-query rows -- the first, the last and rows between -- each computed on its
-own.  Routed heads and kept blocks must be the oracle's (up to a near-tie),
+chunk, HISA and MISA composed with HISA), then the oracle on every query row
+of the decode workloads and on at least 256 rows of the prefill chunk (the
+edges of every query workgroup and random rows), computed for those rows
+alone.  Routed heads and kept blocks must be the oracle's (up to a near-tie),
 selected sets the oracle's up to swaps at the k-th score, and every reported
 score within the score tolerance of the oracle's fp64 score (parity.py)."""
 import numpy as np
@@ -37,8 +38,29 @@ def np_(t):
     return t.cpu().numpy()
 
 
+QWG = 64  # queries per workgroup of the prefill tiling at h = 8
+
+
 def _sample_rows(T):
-    return sorted(set([0, T // 3, (2 * T) // 3, T - 1]))
+    """Every row of the decode workloads; for the 4096-query prefill chunk the
+    first and last row of every 64-query workgroup (which also puts rows on
+    both sides of every 128-key tile edge of the causal boundary) plus
+    seeded random rows, at least 256 in all."""
+    if T <= 64:
+        return list(range(T))
+    rows = set()
+    for q0 in range(0, T, QWG):
+        rows.update((q0, min(q0 + QWG, T) - 1))
+    rng = np.random.default_rng(2024)
+    while len(rows) < 256:
+        rows.add(int(rng.integers(0, T)))
+    return sorted(rows)
+
+
+def _allowed_skips(n_rows):
+    """Rows whose routed heads differ from the oracle's on a near-tie are
+    skipped (their selection is a different, equally valid set)."""
+    return max(1, n_rows // 50)
 
 
 def _sub(case, rows):
@@ -91,7 +113,7 @@ def test_workload_misa(name):
         n = int(case["q_pos"][r]) + 1
         _check_row(idx[r], val[r], o["idx"][j], o["scores"][j], n, k)
         checked += 1
-    assert checked >= len(rows) - 1
+    assert checked >= len(rows) - _allowed_skips(len(rows))
 
 
 def test_workload_dsa_dense():
@@ -174,4 +196,4 @@ def test_workload_hisa(name):
             if i >= 0:
                 assert abs(float(v) - osc[j, i]) <= parity.REL * (abs(osc[j, i]) + sbt)
         checked += 1
-    assert checked >= len(rows) - 1
+    assert checked >= len(rows) - _allowed_skips(len(rows))
