@@ -135,6 +135,16 @@ bool use_prefill(const misa_batch *b, const int32_t *heads, int h) {
   return heads && b->S == 1 && b->T >= kPrefillMinRows && prefill_supported(h, b->Lmax, b->Lmax);
 }
 
+// Key columns per prefill workgroup: about one workgroup per compute unit
+// (one fits at a time: its A rows fill the registers), query tiles x key
+// splits of whole key tiles.
+int prefill_split(int T, int h, int Lmax) {
+  const int nqt = (T + prefill_queries_per_wg(h) - 1) / prefill_queries_per_wg(h);
+  const int nsplit = std::max(1, std::min((Lmax + 1023) / 1024, (256 + nqt / 2) / nqt));
+  const int split = (Lmax + nsplit - 1) / nsplit;
+  return (split + kPrefillKeyTile - 1) / kPrefillKeyTile * kPrefillKeyTile;
+}
+
 PrefillArgs make_prefill_args(const misa_batch *b, const int32_t *heads, int h, float *scores) {
   PrefillArgs p{};
   p.keys = b->keys;
@@ -149,13 +159,66 @@ PrefillArgs make_prefill_args(const misa_batch *b, const int32_t *heads, int h, 
   p.Lmax = b->Lmax;
   p.T = b->T;
   p.ld = b->Lmax;
-  // about one workgroup per compute unit (one fits at a time: its A rows fill
-  // the registers): query tiles x key splits of whole key tiles
-  const int nqt = (b->T + prefill_queries_per_wg(h) - 1) / prefill_queries_per_wg(h);
-  const int nsplit = std::max(1, std::min((b->Lmax + 1023) / 1024, (256 + nqt / 2) / nqt));
-  int split = (b->Lmax + nsplit - 1) / nsplit;
-  p.split = (split + kPrefillKeyTile - 1) / kPrefillKeyTile * kPrefillKeyTile;
+  p.split = prefill_split(b->T, h, b->Lmax);
   return p;
+}
+
+// The prefill chunk's select from threshold lists (tlist.hip): the scores of
+// kTlistSample keys spread over the shortest prefix give every row a lower
+// bound tau of its k-th score; the scoring kernel keeps the scores >= tau in
+// one list per (key split, row) of tcap entries besides the score rows, and
+// one workgroup per row selects from their union.  The score rows are not
+// written: the rows whose lists cannot prove their top-k (a list overflowed,
+// fewer than k scores reached tau) are rescored one by one (score_rows_kernel
+// over the merge's list of them) and take the row select.  Taken
+// for many long rows (where the streamed select would read the whole matrix)
+// when the expected union of a row fits the merge's registers.
+struct TlistLayout {
+  size_t sample, spos, sscore, tau, tcount, tlists, flist, total;
+  int nsplit, tcap;
+  bool on;
+};
+TlistLayout tlist_layout(const misa_batch *b, int h, int k) {
+  TlistLayout L{};
+  const int T = b->T, n = b->Lmax;
+  if (!(b->S == 1 && T >= kRowSelectMinRows && n > kRowSelectMaxShortRow && h >= 1 &&
+        prefill_supported(h, n, n) && prefill_lists_supported(h) && k >= 1 && k <= n))
+    return L;
+  const int split = prefill_split(T, h, n);
+  L.nsplit = (n + split - 1) / split;
+  if (L.nsplit > kMaxTlists) return L;
+  // a row of n columns: tau is the r-th of the row's sample scores with
+  // m = k NS / n and r = m + 6 sqrt(m) + 8 (tlist_tau_kernel), so about
+  // u = r n / NS of its scores reach it, give or take sqrt(r) n / NS
+  const double ns = kTlistSample, m = (double)k * ns / n, r = m + 6.0 * std::sqrt(m) + 8.0;
+  if (r >= ns) return L;
+  const double u = r * n / ns, sd = std::sqrt(r) * n / ns;
+  if (u + 4.0 * sd > 0.9 * kTlistUnionCap) return L;
+  // the merge's register slots: ceil(len / threads) per list
+  if ((u + 4.0 * sd) / kTlistMergeThreads + L.nsplit > kTlistUnionCap / kTlistMergeThreads) return L;
+  // a list takes one split of one row: u split / n hits on average, with
+  // room for rows up to 1.5x as dense (shorter prefixes)
+  const double mu = 1.5 * u * split / n;
+  L.tcap = ((int)std::ceil(mu + 6.0 * std::sqrt(mu) + 32.0) + 7) / 8 * 8;
+  if ((uint64_t)prefill_queries_per_wg(h) * L.tcap * 8 > 0x7FFFFFF0ull) return L;
+  size_t off = 0;
+  L.sample = off;
+  off = align_up(off + (size_t)kTlistSample * MISA_D * sizeof(uint16_t));
+  L.spos = off;
+  off = align_up(off + (size_t)T * sizeof(int32_t));
+  L.sscore = off;
+  off = align_up(off + (size_t)T * kTlistSample * sizeof(float));
+  L.tau = off;
+  off = align_up(off + (size_t)T * sizeof(float));
+  L.tcount = off;
+  off = align_up(off + (size_t)L.nsplit * T * sizeof(uint32_t));
+  L.tlists = off;
+  off = align_up(off + (size_t)L.nsplit * T * L.tcap * sizeof(uint2));
+  L.flist = off;  // the count, then the flagged rows
+  off = align_up(off + (size_t)(T + 1) * sizeof(int32_t));
+  L.total = off;
+  L.on = true;
+  return L;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MISA_OK : MISA_ERR_HIP; }
@@ -234,6 +297,91 @@ ScoreArgs make_score_args(const misa_batch *b, const int32_t *heads, int nh) {
   return s;
 }
 
+// A prefill chunk: the MFMA scoring of prefill.hip, then the select -- from
+// threshold lists when TL.on (the tlist workspace follows the select's),
+// else over the score matrix.  The events bracket the main scoring kernel.
+int prefill_select(const misa_batch *b, const int32_t *heads, int h, int k, int32_t *idx, float *val,
+                   void *ws, const SelectLayout &L, const TlistLayout &TL, hipStream_t st, void *ev_start,
+                   void *ev_stop) {
+  float *sc = (float *)((char *)ws + L.scores);
+  PrefillArgs p = make_prefill_args(b, heads, h, sc);
+  if (!TL.on) {
+    if (launch_score_prefill(p, st, (hipEvent_t)ev_start, (hipEvent_t)ev_stop) != hipSuccess)
+      return MISA_ERR_HIP;
+    return run_select(nullptr, sc, b->T, b->Lmax, b->q_pos, 1, nullptr, k, idx, val, ws, L, st);
+  }
+  char *tw = (char *)ws + L.total;
+  uint16_t *sample = (uint16_t *)(tw + TL.sample);
+  int32_t *spos = (int32_t *)(tw + TL.spos);
+  float *ss = (float *)(tw + TL.sscore);
+  float *tau = (float *)(tw + TL.tau);
+  uint32_t *tcount = (uint32_t *)(tw + TL.tcount);
+  uint2 *tlists = (uint2 *)(tw + TL.tlists);
+  uint32_t *fcount = (uint32_t *)(tw + TL.flist);
+  int32_t *flist = (int32_t *)(tw + TL.flist) + 1;
+  // the sample's scores: the same tiling over kTlistSample keys every row sees
+  if (launch_tlist_gather(b->keys, b->q_pos, b->T, b->Lmax, kTlistSample, sample, spos, fcount, st) !=
+      hipSuccess)
+    return MISA_ERR_HIP;
+  PrefillArgs ps = p;
+  ps.keys = sample;
+  ps.q_pos = spos;
+  ps.scores = ss;
+  ps.seq = 0;
+  ps.Lmax = ps.ld = kTlistSample;
+  ps.split = kTlistSample / 4;  // four key splits: about one workgroup per compute unit at 4096 rows
+  if (launch_score_prefill(ps, st) != hipSuccess) return MISA_ERR_HIP;
+  if (launch_tlist_tau(ss, b->q_pos, b->T, kTlistSample, k, tau, st) != hipSuccess) return MISA_ERR_HIP;
+  // the lists (no score rows)
+  p.tau = tau;
+  p.tlists = tlists;
+  p.tcount = tcount;
+  p.tcap = TL.tcap;
+  if ((p.Lmax + p.split - 1) / p.split != TL.nsplit) return MISA_ERR_HIP;  // layouts out of step
+  if (launch_score_prefill(p, st, (hipEvent_t)ev_start, (hipEvent_t)ev_stop) != hipSuccess)
+    return MISA_ERR_HIP;
+  TlistArgs ta{};
+  ta.tlists = tlists;
+  ta.tcount = tcount;
+  ta.tau = tau;
+  ta.q_pos = b->q_pos;
+  ta.counters = (uint32_t *)((char *)ws + L.counters);
+  ta.idx = idx;
+  ta.val = val;
+  ta.T = b->T;
+  ta.nsplit = TL.nsplit;
+  ta.tcap = TL.tcap;
+  ta.ld = b->Lmax;
+  ta.k = k;
+  ta.flist = flist;
+  ta.fcount = fcount;
+  if (launch_tlist_merge(ta, st) != hipSuccess) return MISA_ERR_HIP;
+  // the rows the lists could not settle (flagged by the merge): their score
+  // rows, then the row select over them
+  ScoreArgs s = make_score_args(b, heads, h);
+  s.scores = sc;
+  s.cand = nullptr;
+  s.ncols = b->Lmax;
+  s.ld = b->Lmax;
+  s.chunk = kMaxScoreChunk;
+  s.rowlist = flist;
+  s.rowcount = fcount;
+  if (launch_score_rows(s, st) != hipSuccess) return MISA_ERR_HIP;
+  TopkArgs t{};
+  t.counters = ta.counters;
+  t.scores = sc;
+  t.row_len = b->q_pos;
+  t.row_len_add = 1;
+  t.idx = idx;
+  t.val = val;
+  t.rows = b->T;
+  t.ld = b->Lmax;
+  t.k = k;
+  t.only_flagged = 1;
+  return hip_status(launch_topk_rowselect(t, st));
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -265,7 +413,8 @@ int misa_workspace_bytes(const misa_batch *b, int32_t op, int32_t B, int32_t h, 
     case MISA_OP_DENSE:
     case MISA_OP_SCORE_TOPK:
       if (k < 1 || k > b->Lmax) return MISA_ERR_SHAPE;
-      *bytes = select_layout(b->T, b->Lmax, k, true).total;
+      *bytes = select_layout(b->T, b->Lmax, k, true).total +
+               (op == MISA_OP_SCORE_TOPK ? tlist_layout(b, h, k).total : 0);
       return MISA_OK;
     case MISA_OP_RERANK:
       if (k < 1 || kc < k || kc > b->Lmax) return MISA_ERR_SHAPE;
@@ -273,7 +422,7 @@ int misa_workspace_bytes(const misa_batch *b, int32_t op, int32_t B, int32_t h, 
       return MISA_OK;
     case MISA_OP_INDEXER:
       if (B < 1 || B > b->Lmax || h < 1 || h > b->H || k < 1 || k > b->Lmax) return MISA_ERR_SHAPE;
-      *bytes = route_bytes(b, B) + select_layout(b->T, b->Lmax, k, true).total;
+      *bytes = route_bytes(b, B) + select_layout(b->T, b->Lmax, k, true).total + tlist_layout(b, h, k).total;
       return MISA_OK;
     case MISA_OP_TOPK:
       if (k < 1) return MISA_ERR_SHAPE;
@@ -400,15 +549,10 @@ int misa_score_topk_ev(const misa_batch *b, const int32_t *heads, int32_t h, int
   if (heads && (h < 1 || h > b->H)) return MISA_ERR_SHAPE;
   if (k < 1 || k > b->Lmax) return MISA_ERR_SHAPE;
   const SelectLayout L = select_layout(b->T, b->Lmax, k, true);
-  if (ws_bytes < L.total) return MISA_ERR_WORKSPACE;
-  if (use_prefill(b, heads, h)) {
-    float *sc = (float *)((char *)ws + L.scores);
-    if (launch_score_prefill(make_prefill_args(b, heads, h, sc), (hipStream_t)stream,
-                             (hipEvent_t)ev_start, (hipEvent_t)ev_stop) != hipSuccess)
-      return MISA_ERR_HIP;
-    return run_select(nullptr, sc, b->T, b->Lmax, b->q_pos, 1, nullptr, k, idx, val, ws, L,
-                      (hipStream_t)stream);
-  }
+  const TlistLayout TL = heads ? tlist_layout(b, h, k) : TlistLayout{};
+  if (ws_bytes < L.total + TL.total) return MISA_ERR_WORKSPACE;
+  if (use_prefill(b, heads, h))
+    return prefill_select(b, heads, h, k, idx, val, ws, L, TL, (hipStream_t)stream, ev_start, ev_stop);
   ScoreArgs s = make_score_args(b, heads, heads ? h : b->H);
   s.scores = (float *)((char *)ws + L.scores);
   s.cand = nullptr;
@@ -455,7 +599,8 @@ int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t
   if (!a16(ws)) return MISA_ERR_UNSUPPORTED;
   const size_t rbytes = route_bytes(b, B);
   const SelectLayout L = select_layout(b->T, b->Lmax, k, true);
-  if (ws_bytes < rbytes + L.total) return MISA_ERR_WORKSPACE;
+  const TlistLayout TL = tlist_layout(b, h, k);
+  if (ws_bytes < rbytes + L.total + TL.total) return MISA_ERR_WORKSPACE;
   void *sws = (char *)ws + rbytes;
   const RouteArgs ra = make_route_args(b, pooled, B, h, mode, heads, head_score, ws);
   // many queries of one sequence: the tiled router writes the heads; the
@@ -467,14 +612,8 @@ int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t
                   : prefill    ? launch_route(ra, (hipStream_t)stream)
                                : launch_route_partial(ra, (hipStream_t)stream);
   if (re != hipSuccess) return MISA_ERR_HIP;
-  if (prefill) {
-    float *sc = (float *)((char *)sws + L.scores);
-    if (launch_score_prefill(make_prefill_args(b, heads, h, sc), (hipStream_t)stream,
-                             (hipEvent_t)ev_start, (hipEvent_t)ev_stop) != hipSuccess)
-      return MISA_ERR_HIP;
-    return run_select(nullptr, sc, b->T, b->Lmax, b->q_pos, 1, nullptr, k, idx, val, sws, L,
-                      (hipStream_t)stream);
-  }
+  if (prefill)
+    return prefill_select(b, heads, h, k, idx, val, sws, L, TL, (hipStream_t)stream, ev_start, ev_stop);
   ScoreArgs s = make_score_args(b, heads, h);
   if (in_prologue) {  // heads come from the router's partial sums
     s.heads = nullptr;

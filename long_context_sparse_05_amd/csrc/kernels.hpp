@@ -38,6 +38,10 @@ struct ScoreArgs {
   int nparts, mode;
   int32_t *heads_out;
   float *g_out;
+  // A row list (optional; direct rows, nh <= 16): the rows rowlist[0 ..
+  // *rowcount) are scored instead of rows 0 .. T-1 (T bounds the count).
+  const int32_t *rowlist;
+  const uint32_t *rowcount;
   int nh, H, Lmax, T;
   int ncols, ld, chunk;
 };
@@ -59,6 +63,16 @@ struct PrefillArgs {
   int seq;                 // the one sequence all rows read
   int h, H, Lmax, T, ld;
   int split;               // key columns per workgroup, a multiple of 64
+  // Threshold lists (optional, tau != nullptr): instead of the score rows
+  // (scores is not written), every score >= tau[t] goes to tlists
+  // [nsplit][T][tcap] as (score bits, column) -- list [split][t] holds row
+  // t's hits in the columns of that split, in no set order -- and the count
+  // of hits (which may exceed tcap: the list overflowed) to tcount
+  // [nsplit][T].
+  const float *tau;
+  uint2 *tlists;
+  uint32_t *tcount;
+  int tcap;
 };
 // key tile of the prefill kernel: PrefillArgs::split must be a multiple
 constexpr int kPrefillKeyTile = 128;
@@ -66,6 +80,7 @@ hipError_t launch_score_prefill(const PrefillArgs &a, hipStream_t st, hipEvent_t
                                 hipEvent_t ev1 = nullptr);
 int prefill_queries_per_wg(int h);
 bool prefill_supported(int h, int ld, int Lmax);  // the launch shape fits h, the row length and the keys
+bool prefill_lists_supported(int h);              // the tiling for h heads can write threshold lists
 
 // Per-row top-k selection (topk.hip).
 struct TopkArgs {
@@ -94,6 +109,29 @@ constexpr int kStreamSelectMinCols = 16384;   // rows of kStreamSelectMinCols..k
 constexpr int kStreamSelectMaxCols = 131072;  // columns take the streamed select
 constexpr int kStreamSelectCap = 4096;        // its list of bracketed columns, per row
 constexpr int kStreamSelectSample = 4096;     // its sample, per row
+
+// The prefill chunk's top-k from threshold lists (tlist.hip).
+struct TlistArgs {
+  const uint2 *tlists;     // [nsplit][T][tcap] (score bits, column)
+  const uint32_t *tcount;  // [nsplit][T] hits (> tcap: the list overflowed)
+  const float *tau;        // [T] the lists' lower bound
+  const int32_t *q_pos;    // [T]
+  uint32_t *counters;      // [T][kRowCounters]: counter 7 = 1 flags the row for the row select
+  int32_t *flist;          // [T] the flagged rows, *fcount of them (zeroed by tlist_gather_kernel)
+  uint32_t *fcount;
+  int32_t *idx;            // [T][k]
+  float *val;              // [T][k] or nullptr
+  int T, nsplit, tcap, ld, k;
+};
+constexpr int kMaxTlists = 64;         // lists (key splits) per row
+constexpr int kTlistSample = 2048;     // sampled keys that set tau
+constexpr int kTlistUnionCap = 8192;   // union entries the merge holds (in registers)
+constexpr int kTlistMergeThreads = 256;
+hipError_t launch_tlist_gather(const uint16_t *keys, const int32_t *q_pos, int T, int Lmax, int ns,
+                               uint16_t *sample, int32_t *spos, uint32_t *fcount, hipStream_t st);
+hipError_t launch_tlist_tau(const float *ss, const int32_t *q_pos, int T, int ns, int k, float *tau,
+                            hipStream_t st);
+hipError_t launch_tlist_merge(const TlistArgs &a, hipStream_t st);
 
 // Block mean-pool (pool.hip).
 hipError_t launch_pool(const uint16_t *keys, const int32_t *seq_lens, int S, int Lmax,

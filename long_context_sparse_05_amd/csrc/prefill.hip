@@ -44,6 +44,7 @@
 namespace misa {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -61,7 +62,14 @@ template <int E> using epi_t = std::integral_constant<int, E>;
 // whole number of tiles (the host launches only such workgroups here);
 // GEN = true: ragged workgroups, every store checked.  qtile0 / split0 offset
 // the grid into the workgroup space.
-template <int HP, int RT, int NW, int KT, bool GEN>
+// LISTS: instead of the score rows, every score >= tau[row] goes to the
+// row's threshold list for this key split (kernels.hpp, PrefillArgs::tau) as
+// (score bits, column): the 32 lanes holding a row's columns place their hits
+// side by side (positions from a ballot) after those of the earlier column
+// blocks, so a row's list is one contiguous run and a store touches one or
+// two cache lines; its length (which may pass the capacity: the list
+// overflowed) is written at the end.
+template <int HP, int RT, int NW, int KT, bool GEN, bool LISTS>
 __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, int qtile0, int split0) {
   constexpr int QPT = 32 / HP;                  // queries per 32-row tile
   constexpr int QPL = 16 / HP;                  // queries per lane (per tile)
@@ -70,7 +78,11 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
   constexpr int NB = KT / 32;                   // 32-key column blocks per tile
   constexpr int NDMA = KT / (4 * NW);           // 16-byte DMA loads per thread per tile
   constexpr int TB = KT * 256;                  // bytes per key tile
-  constexpr int OUT = RT * QPL;                 // score stores per lane per column block
+  constexpr int OUT = RT * QPL;                 // scores per lane per column block
+  // stores per lane per column block that the waits count: the score rows'
+  // stores.  List stores are issued only where a lane has a hit and are not
+  // counted: with lists every wait is for all outstanding operations.
+  constexpr int VMO = LISTS ? 0 : OUT;
   static_assert(NDMA * 4 * NW == KT && NW % 4 == 0 && NB == 4, "tile shape");
   // the two key-tile buffers are separate arrays so that the compiler can
   // tell reads of one from DMA writes into the other
@@ -104,6 +116,8 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
   uint32_t rowo[RT][QPL];
   int lim[RT][QPL];   // position - l32: key kb + l32 is in the prefix iff kb <= lim
   bool rowok[RT][QPL];
+  float tau[RT][QPL];      // threshold-list cut of the lane's rows (LISTS)
+  uint32_t lcnt[RT][QPL];  // hits of the lane's row so far (the same in the 32 lanes of the row)
   // The lane's rows: A row l32 of tile rt is (query tA, head slot sA); its
   // accumulator rows r are (query tile_q0 + g*QPL + r/HP, slot r%HP).  Every
   // index is clamped so that all loads of a round are issued together (two
@@ -148,6 +162,10 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
       rowo[rt][qq] = (uint32_t)(((t - qt0) * a.ld + l32) * 4);
       rowok[rt][qq] = t < a.T;
       lim[rt][qq] = t < a.T ? pos[rt][qq] - l32 : INT_MIN;
+      if constexpr (LISTS) {
+        tau[rt][qq] = a.tau[min(t, Tm)];
+        lcnt[rt][qq] = 0;
+      }
     }
   }
 
@@ -185,6 +203,18 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
   // the workgroup's score rows (at most QWG rows of ld floats: 32-bit offsets)
   const __amdgpu_buffer_rsrc_t srs =
       __builtin_amdgcn_make_buffer_rsrc((void *)wg_rows, (short)0, (int)((uint32_t)QWG * a.ld * 4u), 0x00020000);
+  // the workgroup's threshold lists for this split: rows qt0.. of
+  // [split][T][tcap] entries
+  const int split_id = blockIdx.x + split0;
+  uint2 *const wg_lists = LISTS ? a.tlists + ((size_t)split_id * a.T + qt0) * a.tcap : nullptr;
+  const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)wg_lists, (short)0, LISTS ? (int)((uint32_t)min(QWG, a.T - qt0) * (uint32_t)a.tcap * 8u) : 0,
+      0x00020000);
+  // the first byte of the list of the lane's row (rt, qq): row
+  // (wave RT + rt) QPT + g QPL + qq of the workgroup
+  const uint32_t lrow = LISTS ? (uint32_t)a.tcap * 8u : 0u;
+  const uint32_t lb0 = LISTS ? (uint32_t)((wave * RT * QPT + g * QPL) * a.tcap * 8) : 0u;
+  auto lbase = [&](int rt, int qq) { return lb0 + (uint32_t)(rt * QPT + qq) * lrow; };
   const f32x16 zero = {};
   f32x16 acc[2][RT];
   uint4 bfr[8];
@@ -213,13 +243,37 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
           sc[o] = hs == 0 ? wv[rt][r] * x : fmaf(wv[rt][r], x, sc[o]);
           if (hs == HP - 1) {
             const int ort = o / QPL, oq = o % QPL;
+            bool in = true;  // the column is in the row's prefix (and in range)
             if (EPI == kEpiFull) {
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc[o]), srs, rowo[ort][oq], kbp * 4, 0);
+              if (!LISTS)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc[o]), srs, rowo[ort][oq], kbp * 4, 0);
             } else if (EPI == kEpiCausal) {
-              const float y = kbp <= lim[ort][oq] ? sc[o] : -INFINITY;
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), srs, rowo[ort][oq], kbp * 4, 0);
-            } else if (rowok[ort][oq] && kbp + l32 < k1) {
-              *(float *)(wg_rows + (size_t)kbp * 4 + rowo[ort][oq]) = kbp <= lim[ort][oq] ? sc[o] : -INFINITY;
+              in = kbp <= lim[ort][oq];
+              const float y = in ? sc[o] : -INFINITY;
+              if (!LISTS) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), srs, rowo[ort][oq], kbp * 4, 0);
+            } else {
+              in = rowok[ort][oq] && kbp + l32 < k1 && kbp <= lim[ort][oq];
+              if (!LISTS && rowok[ort][oq] && kbp + l32 < k1)
+                *(float *)(wg_rows + (size_t)kbp * 4 + rowo[ort][oq]) = in ? sc[o] : -INFINITY;
+            }
+            if constexpr (LISTS) {
+              const bool hit = in && sc[o] >= tau[ort][oq];
+              // the hit's place among its row's hits of this block: lanes
+              // 0..31 hold row g = 0, lanes 32..63 row g = 1
+              const uint64_t hm = __ballot(hit);
+              const uint32_t hlo = (uint32_t)hm, hhi = (uint32_t)(hm >> 32);
+              const uint32_t below =
+                  __builtin_amdgcn_mbcnt_hi(hhi, __builtin_amdgcn_mbcnt_lo(hlo, 0u)) - (g ? (uint32_t)__popc(hlo) : 0u);
+              const uint32_t slot = lcnt[ort][oq] + below;
+              lcnt[ort][oq] += g ? (uint32_t)__popc(hhi) : (uint32_t)__popc(hlo);
+              if (hit && slot < (uint32_t)a.tcap) {
+                const u32x2 ent = {__float_as_uint(sc[o]), (uint32_t)(kbp + l32)};
+                const uint32_t off = lbase(ort, oq) + slot * 8u;
+                if (EPI == kEpiGeneric)
+                  *(u32x2 *)((char *)wg_lists + off) = ent;
+                else
+                  __builtin_amdgcn_raw_buffer_store_b64(ent, lrs, off, 0, 0);
+              }
             }
           }
         }
@@ -244,9 +298,9 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
     if (PE == kEpiGeneric || CE == kEpiGeneric) {
       PF_WAIT_VM(0);
     } else if (PE == kEpiNone) {
-      PF_WAIT_VM((NB - 2) * OUT < 63 ? (NB - 2) * OUT : 63);
+      PF_WAIT_VM((NB - 2) * VMO < 63 ? (NB - 2) * VMO : 63);
     } else {
-      PF_WAIT_VM(NB * OUT < 63 ? NB * OUT : 63);
+      PF_WAIT_VM(NB * VMO < 63 ? NB * VMO : 63);
     }
     __syncthreads();
     if (it + 2 < ntile) dma_tile(it + 2, cur_b{});
@@ -290,6 +344,16 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
     f32x16 dummy[RT];
     block(dummy, acc[1], b0{}, std::integral_constant<int, 0>{}, kbp, epi_t<E>{});
   }
+  if constexpr (LISTS) {  // the rows' hit counts: [split][T]
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int qq = 0; qq < QPL; ++qq) {
+        const int t = qt0 + (wave * RT + rt) * QPT + g * QPL + qq;
+        if (l32 == 0 && t < a.T) a.tcount[(size_t)split_id * a.T + t] = lcnt[rt][qq];
+      }
+  }
+  if (LISTS) return;  // no score rows
   // columns of this split past every query of the workgroup
   const int cstart = min(k1, k0 + ntile * KT);
   for (int qi = 0; qi < QWG; ++qi) {
@@ -302,7 +366,7 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
 constexpr int kPfWaves = 8, kPfKeys = kPrefillKeyTile;
 constexpr int pf_rt(int hp) { return hp >= 4 ? 2 : 1; }
 
-template <int HP>
+template <int HP, bool LISTS>
 static hipError_t launch_hp(const PrefillArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   constexpr int RT = pf_rt(HP);
   constexpr int QWG = kPfWaves * RT * (32 / HP);
@@ -325,11 +389,11 @@ static hipError_t launch_hp(const PrefillArgs &a, hipStream_t st, hipEvent_t ev0
     else
       hipLaunchKernelGGL(kernel, grid, dim3(kPfWaves * 64), 0, st, a, qtile0, split0);
   };
-  if (l0) launch(0, score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, false>, dim3(ns_full, nq_full), 0, 0);
+  if (l0) launch(0, score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, false, LISTS>, dim3(ns_full, nq_full), 0, 0);
   if (l1)  // the ragged last row of query tiles, all splits
-    launch(1, score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, true>, dim3(nsplit, 1), nq_full, 0);
+    launch(1, score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, true, LISTS>, dim3(nsplit, 1), nq_full, 0);
   if (l2)  // the ragged last split, whole query tiles
-    launch(2, score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, true>, dim3(1, nq_full), 0, ns_full);
+    launch(2, score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, true, LISTS>, dim3(1, nq_full), 0, ns_full);
   if (first < 0) {  // nothing to launch: the events mark the empty interval
     if (ev0 && hipEventRecord(ev0, st) != hipSuccess) return hipErrorInvalidValue;
     if (ev1 && hipEventRecord(ev1, st) != hipSuccess) return hipErrorInvalidValue;
@@ -347,13 +411,29 @@ bool prefill_supported(int h, int ld, int Lmax) {
          (uint64_t)Lmax * 256 <= 0x7FFFFFFFull;
 }
 
-hipError_t launch_score_prefill(const PrefillArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  if (a.h <= 1) return launch_hp<1>(a, st, ev0, ev1);
-  if (a.h <= 2) return launch_hp<2>(a, st, ev0, ev1);
-  if (a.h <= 4) return launch_hp<4>(a, st, ev0, ev1);
-  if (a.h <= 8) return launch_hp<8>(a, st, ev0, ev1);
-  if (a.h <= 16) return launch_hp<16>(a, st, ev0, ev1);
+// The threshold lists cost two registers per (lane, row): the tilings with
+// one, two or four head slots per query (8 to 16 rows per lane) have none to
+// spare and run without lists.
+bool prefill_lists_supported(int h) { return h >= 5 && h <= 16; }
+
+template <bool LISTS>
+static hipError_t launch_lists(const PrefillArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  if constexpr (!LISTS) {
+    if (a.h <= 1) return launch_hp<1, false>(a, st, ev0, ev1);
+    if (a.h <= 2) return launch_hp<2, false>(a, st, ev0, ev1);
+    if (a.h <= 4) return launch_hp<4, false>(a, st, ev0, ev1);
+  }
+  if (a.h >= 5 && a.h <= 8) return launch_hp<8, LISTS>(a, st, ev0, ev1);
+  if (a.h >= 9 && a.h <= 16) return launch_hp<16, LISTS>(a, st, ev0, ev1);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_score_prefill(const PrefillArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  if (!a.tau) return launch_lists<false>(a, st, ev0, ev1);
+  if (!prefill_lists_supported(a.h) || !a.tlists || !a.tcount || a.tcap < 1 ||
+      (uint64_t)prefill_queries_per_wg(a.h) * a.tcap * 8 > 0x7FFFFFF0ull)
+    return hipErrorInvalidValue;
+  return launch_lists<true>(a, st, ev0, ev1);
 }
 
 }  // namespace misa

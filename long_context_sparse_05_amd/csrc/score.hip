@@ -43,8 +43,9 @@ constexpr int score_waves() {
   return HT == 1 && !GATHER ? 8 : 4;
 }
 
+// One (chunk, row) of the scoring: the body of score_rows_kernel.
 template <int HT, bool GATHER, bool ROUTE, int U, int NW>
-__global__ __launch_bounds__(NW * 64) void score_rows_kernel(ScoreArgs a) {
+__device__ __forceinline__ void score_row_chunk(const ScoreArgs &a, const int t) {
   constexpr int NT = NW * 64;
   static_assert(!(ROUTE && GATHER), "the router prologue serves direct rows");
   __shared__ uint32_t lds_hist[kHistBins];
@@ -55,7 +56,6 @@ __global__ __launch_bounds__(NW * 64) void score_rows_kernel(ScoreArgs a) {
   __shared__ int32_t ctok[GATHER ? kMaxScoreChunk : 1];  // the chunk's candidate tokens
   __shared__ float csc[kMaxScoreChunk];                   // the chunk's scores
   __shared__ uint32_t lsh[2 * NW + 9];                    // scan scratch; [2 NW + 8] valid-entry count
-  const int t = blockIdx.y;
   const int lane = lane_id();
   // wave-uniform, and known to be: the step loop below branches on scalars
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -263,18 +263,48 @@ __global__ __launch_bounds__(NW * 64) void score_rows_kernel(ScoreArgs a) {
   }
 }
 
+// Grid (chunks, rows): workgroup (x, y) scores chunk x of row y -- or, with
+// a row list (RLIST), of rows rowlist[y], rowlist[y + gridDim.y], ... below
+// *rowcount, one after another.
+template <int HT, bool GATHER, bool ROUTE, int U, int NW, bool RLIST>
+__global__ __launch_bounds__(NW * 64) void score_rows_kernel(ScoreArgs a) {
+  if constexpr (RLIST) {
+    const uint32_t nrows = *a.rowcount;
+    for (uint32_t y = blockIdx.y; y < nrows; y += gridDim.y) {
+      score_row_chunk<HT, GATHER, ROUTE, U, NW>(a, a.rowlist[y]);
+      __syncthreads();  // the next row reuses the shared memory
+    }
+  } else {
+    score_row_chunk<HT, GATHER, ROUTE, U, NW>(a, (int)blockIdx.y);
+  }
+}
+
+// workgroup rows of a row-list launch (each walks its share of the list)
+constexpr int kRowListGrid = 64;
+
 template <int HT, bool GATHER, bool ROUTE>
 static hipError_t launch_ht(const ScoreArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+  if (a.rowlist) {  // (at most 16 heads: the rows a prefill chunk's select rescores)
+    if constexpr (HT == 1 && !GATHER && !ROUTE) {
+      if (!a.rowcount || ev0 || ev1 || a.chunk > kMaxScoreChunk) return hipErrorInvalidValue;
+      constexpr int U = 2, NW = score_waves<HT, false>();
+      const dim3 grid((a.ncols + a.chunk - 1) / a.chunk, a.T < kRowListGrid ? a.T : kRowListGrid);
+      hipLaunchKernelGGL((score_rows_kernel<HT, false, false, U, NW, true>), grid, dim3(NW * 64), 0, st, a);
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
   dim3 grid((a.ncols + a.chunk - 1) / a.chunk, a.T);
   // two 16-key tiles per wave step: fewer registers, more waves per CU
   constexpr int U = 2;
   constexpr int NW = score_waves<HT, GATHER>();
   if (a.chunk > kMaxScoreChunk) return hipErrorInvalidValue;
   if (ev0 || ev1)  // the measurement hook: events stamped with the kernel's begin and end
-    hipExtLaunchKernelGGL((score_rows_kernel<HT, GATHER, ROUTE, U, NW>), grid, dim3(NW * 64), 0, st, ev0, ev1,
-                          0, a);
+    hipExtLaunchKernelGGL((score_rows_kernel<HT, GATHER, ROUTE, U, NW, false>), grid, dim3(NW * 64), 0, st, ev0,
+                          ev1, 0, a);
   else
-    hipLaunchKernelGGL((score_rows_kernel<HT, GATHER, ROUTE, U, NW>), grid, dim3(NW * 64), 0, st, a);
+    hipLaunchKernelGGL((score_rows_kernel<HT, GATHER, ROUTE, U, NW, false>), grid, dim3(NW * 64), 0, st, a);
   return hipGetLastError();
 }
 

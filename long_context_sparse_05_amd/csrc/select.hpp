@@ -90,6 +90,14 @@ __device__ __forceinline__ Thresh threshold_from_lds(const uint32_t *lh, uint32_
   return th;
 }
 
+// A selection key that orders (score, token) pairs: the score's order key in
+// the high word and the complemented token in the low word, so that of equal
+// scores the lower token ranks higher (the row's ties are broken by token).
+__device__ __forceinline__ uint64_t composite(uint32_t key, int tok) {
+  return ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)tok);
+}
+
+
 // ------------------------------------------------------- chunk candidate lists
 // The two-stage top-k of few long rows.  A row is cut into chunks (one per
 // workgroup of the kernel that produces its scores); each chunk keeps a

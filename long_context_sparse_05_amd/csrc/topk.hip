@@ -64,10 +64,6 @@ __device__ __forceinline__ bool lds_append(bool pred, uint32_t *counter, uint32_
   return pred;
 }
 
-__device__ __forceinline__ uint64_t composite(uint32_t key, int tok) {
-  return ((uint64_t)key << 32) | (uint32_t)(~(uint32_t)tok);
-}
-
 // Resolve the candidates of the threshold digit: 8-bit digit passes over
 // LDS histograms of the remaining 52 composite-key bits, emitting every key
 // above each pass's crossing digit (wave-aggregated LDS atomics for the

@@ -81,6 +81,29 @@ def test_workspace_sizes(lib):
     assert ws_bytes(lib, b, abi.MISA_OP_HISA, B=64, k=8, kc=16)[1] >= 4 * 16 * 64 * 4
 
 
+def test_prefill_chunk_workspace_holds_the_threshold_lists(lib):
+    """A prefill chunk (one sequence, many long rows) with a tiling that
+    writes threshold lists needs room for them beyond the score rows; the
+    tilings without lists (h <= 4), dense scoring, short rows and
+    decode batches do not."""
+    chunk = batch(S=1, Lmax=65536, T=4096, H=64)
+    score_rows = 4096 * 65536 * 4
+    plain = ws_bytes(lib, chunk, abi.MISA_OP_DENSE, k=2048)[1]
+    assert plain >= score_rows
+    for h in (5, 8, 16):
+        with_lists = ws_bytes(lib, chunk, abi.MISA_OP_SCORE_TOPK, h=h, k=2048)[1]
+        assert with_lists > plain, h
+        assert ws_bytes(lib, chunk, abi.MISA_OP_INDEXER, B=64, h=h, k=2048)[1] > with_lists
+    for h in (1, 2, 3, 4):
+        assert ws_bytes(lib, chunk, abi.MISA_OP_SCORE_TOPK, h=h, k=2048)[1] == plain, h
+    short = batch(S=1, Lmax=8192, T=4096, H=64)
+    assert (ws_bytes(lib, short, abi.MISA_OP_SCORE_TOPK, h=8, k=512)[1]
+            == ws_bytes(lib, short, abi.MISA_OP_DENSE, k=512)[1])
+    decode = batch(S=16, Lmax=131072, T=16, H=64)
+    assert (ws_bytes(lib, decode, abi.MISA_OP_SCORE_TOPK, h=8, k=2048)[1]
+            == ws_bytes(lib, decode, abi.MISA_OP_DENSE, k=2048)[1])
+
+
 def test_validation_before_any_hip_call(lib):
     P = ctypes.c_void_p
     F = P(FAKE)
