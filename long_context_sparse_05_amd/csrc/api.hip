@@ -188,9 +188,9 @@ TlistLayout tlist_layout(const misa_batch *b, int h, int k) {
   L.nsplit = (n + split - 1) / split;
   if (L.nsplit > kMaxTlists) return L;
   // a row of n columns: tau is the r-th of the row's sample scores with
-  // m = k NS / n and r = m + 6 sqrt(m) + 8 (tlist_tau_kernel), so about
+  // m = k NS / n and r = m + sigma sqrt(m) + 8 (tlist_tau_kernel), so about
   // u = r n / NS of its scores reach it, give or take sqrt(r) n / NS
-  const double ns = kTlistSample, m = (double)k * ns / n, r = m + 6.0 * std::sqrt(m) + 8.0;
+  const double ns = kTlistSample, m = (double)k * ns / n, r = m + kTlistSigma * std::sqrt(m) + 8.0;
   if (r >= ns) return L;
   const double u = r * n / ns, sd = std::sqrt(r) * n / ns;
   if (u + 4.0 * sd > 0.9 * kTlistUnionCap) return L;

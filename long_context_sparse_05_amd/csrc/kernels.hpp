@@ -125,6 +125,10 @@ struct TlistArgs {
 };
 constexpr int kMaxTlists = 64;         // lists (key splits) per row
 constexpr int kTlistSample = 2048;     // sampled keys that set tau
+// tau is the sample's r-th largest score, r = m + kTlistSigma sqrt(m) + 8 for
+// m = k NS / n: fewer than k of the row's scores reach it only kTlistSigma
+// standard deviations out (unstructured scores)
+constexpr float kTlistSigma = 4.f;
 constexpr int kTlistUnionCap = 8192;   // union entries the merge holds (in registers)
 constexpr int kTlistMergeThreads = 256;
 hipError_t launch_tlist_gather(const uint16_t *keys, const int32_t *q_pos, int T, int Lmax, int ns,

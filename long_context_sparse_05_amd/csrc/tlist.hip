@@ -15,17 +15,18 @@
 //  2. the prefill scoring kernel scores every row against that sample
 //     (the same MFMA tiling, NS columns);
 //  3. tlist_tau_kernel takes, per row, the r-th largest sample score with
-//     r = m + 6 sqrt(m) + 8 for m = k NS / n_row -- on unstructured scores
-//     the number of row scores at or above it is k n / NS on average and far
-//     more than k with overwhelming probability;
-//  4. the full scoring pass writes its score rows as usual and also every
-//     score >= tau to fixed per-(row, split, column-lane) slots (prefill.hip);
+//     r = m + 4 sqrt(m) + 8 for m = k NS / n_row: about r n / NS of the
+//     row's scores reach it, and fewer than k only four standard deviations
+//     out on unstructured scores;
+//  4. the full scoring pass writes no score rows: every score >= tau goes
+//     to the row's list for its key split (prefill.hip);
 //  5. tlist_merge_kernel, one workgroup per row: the union of the row's
-//     slots is exactly the set of its scores >= tau; when none overflowed and
-//     it holds at least k entries, its top-k is the row's top-k, taken as in
-//     the chunk-list merge (bins over the union's key range, the crossing
-//     bin ranked).  Otherwise the row's flag is set and the row select runs
-//     on the score row (topk_flagged_kernel).
+//     lists is exactly the set of its scores >= tau; when none overflowed
+//     and it holds at least k entries, its top-k is the row's top-k, found
+//     by radix digits of the composite (score, column) keys.  Otherwise the
+//     row goes on the merge's list of flagged rows, which are rescored one
+//     by one (score_rows_kernel) and take the row select
+//     (topk_flagged_kernel).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "select.hpp"
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(256) void tlist_tau_kernel(const float *ss, const i
   if (t >= T) return;  // wave-uniform
   const float n = (float)max(q_pos[t], 0) + 1.f;
   const float m = (float)k * (float)NS / n;
-  const float rf = ceilf(m + 6.f * sqrtf(m) + 8.f);
+  const float rf = ceilf(m + kTlistSigma * sqrtf(m) + 8.f);
   if (rf >= (float)NS) {
     if (lane == 0) tau[t] = -INFINITY;
     return;
@@ -176,8 +177,10 @@ __global__ __launch_bounds__(kTmThreads) void tlist_merge_kernel(TlistArgs a) {
       const uint32_t first = (uint32_t)__builtin_amdgcn_readlane((int)my_first, l);
       const uint32_t len = (uint32_t)__builtin_amdgcn_readlane((int)my_len, l);
       const uint32_t j = (starts ? (uint32_t)u - first : 0u) * NT + tid;
-      if (u < (int)slots && j < len) valid |= 1u << u;
-      e[u] = a.tlists[((size_t)l * a.T + r) * a.tcap + min(j, (uint32_t)a.tcap - 1u)];
+      const bool v = u < (int)slots && j < len;
+      if (v) valid |= 1u << u;
+      // (a slot without an entry reads the list's first: one cache line for all)
+      e[u] = a.tlists[((size_t)l * a.T + r) * a.tcap + (v ? j : 0u)];
     }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -250,34 +253,29 @@ __global__ __launch_bounds__(kTmThreads) void tlist_merge_kernel(TlistArgs a) {
   }
   __syncthreads();
   const uint64_t kth = ((const uint64_t *)red)[0];
-  // every key >= K: exactly kk of them, placed in the histogram's words at
-  // their output positions (2048 at a time) and written out from there
-  uint32_t sel = 0;
+  // every key >= K: exactly kk of them.  Output order is free: wave w's
+  // selected entries of slot u follow those of its slots < u, the waves'
+  // runs one after another, so each store instruction writes one short run.
+  uint32_t wtot = 0;
 #pragma unroll
   for (int u = 0; u < PER; ++u)
-    if (((valid >> u) & 1u) && ck[u] >= kth) sel |= 1u << u;
-  const uint32_t mine = (uint32_t)__popc(sel);
-  uint32_t tot;
-  const uint32_t pos0 = block_scan<NT>(mine, sh, tot) - mine;
-  constexpr uint32_t STG = NB / 2;  // 64-bit entries the histogram's words hold
-  uint64_t *stg = (uint64_t *)lh;
-  for (uint32_t base = 0; base < kk; base += STG) {
-    uint32_t pos = pos0;
+    wtot += (uint32_t)__popcll(__ballot(((valid >> u) & 1u) && ck[u] >= kth));
+  const int wave = tid >> 6;
+  if (lane == 0) sh[wave] = wtot;
+  __syncthreads();
+  uint32_t base = 0;
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      if ((sel >> u) & 1u) {
-        if (pos >= base && pos < base + STG) stg[pos - base] = ck[u];
-        ++pos;
-      }
+  for (int w = 0; w < NW; ++w) base += w < wave ? sh[w] : 0u;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const bool s_u = ((valid >> u) & 1u) && ck[u] >= kth;
+    const uint64_t m = __ballot(s_u);
+    if (s_u) {
+      const uint32_t pos = base + lanes_below(m);
+      irow[pos] = (int32_t)(~(uint32_t)ck[u]);
+      if (vrow) vrow[pos] = key_to_float((uint32_t)(ck[u] >> 32));
     }
-    __syncthreads();
-    const uint32_t nout = min(kk - base, STG);
-    for (uint32_t i = tid; i < nout; i += NT) {
-      const uint64_t c = stg[i];
-      irow[base + i] = (int32_t)(~(uint32_t)c);
-      if (vrow) vrow[base + i] = key_to_float((uint32_t)(c >> 32));
-    }
-    __syncthreads();
+    base += (uint32_t)__popcll(m);
   }
   for (int i = (int)kk + tid; i < a.k; i += NT) {
     irow[i] = -1;
