@@ -128,11 +128,13 @@ HisaLayout hisa_layout(const misa_batch *b, int B, int m, int k) {
   return H;
 }
 
-// Many queries of one sequence with a few routed heads: the dense MFMA
-// tiling of prefill.hip.  Otherwise each query row streams the keys itself.
+// Many queries of one sequence, routed (h heads) or dense (every head,
+// heads == nullptr): the MFMA tiling of prefill.hip, for up to 64 head slots
+// per query.  Otherwise each query row streams the keys itself.
 constexpr int kPrefillMinRows = 64;
 bool use_prefill(const misa_batch *b, const int32_t *heads, int h) {
-  return heads && b->S == 1 && b->T >= kPrefillMinRows && prefill_supported(h, b->Lmax, b->Lmax);
+  const int nh = heads ? h : b->H;
+  return b->S == 1 && b->T >= kPrefillMinRows && prefill_supported(nh, b->Lmax, b->Lmax);
 }
 
 // Key columns per prefill workgroup: about one workgroup per compute unit
@@ -146,6 +148,7 @@ int prefill_split(int T, int h, int Lmax) {
 }
 
 PrefillArgs make_prefill_args(const misa_batch *b, const int32_t *heads, int h, float *scores) {
+  if (!heads) h = b->H;  // dense: every head
   PrefillArgs p{};
   p.keys = b->keys;
   p.q = b->q;

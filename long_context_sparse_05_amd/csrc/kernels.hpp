@@ -58,7 +58,7 @@ struct PrefillArgs {
   const uint16_t *q;       // bf16 [T][H][128]
   const float *w;          // [T][H]
   const int32_t *q_pos;    // [T]
-  const int32_t *heads;    // [T][h], h <= 16
+  const int32_t *heads;    // [T][h] routed heads, or nullptr: slot j is head j (dense, h = H)
   float *scores;           // [T][ld]
   int seq;                 // the one sequence all rows read
   int h, H, Lmax, T, ld;
@@ -76,6 +76,7 @@ struct PrefillArgs {
 };
 // key tile of the prefill kernel: PrefillArgs::split must be a multiple
 constexpr int kPrefillKeyTile = 128;
+constexpr int kPrefillMaxHeads = 64;  // head slots per query the tiling takes
 hipError_t launch_score_prefill(const PrefillArgs &a, hipStream_t st, hipEvent_t ev0 = nullptr,
                                 hipEvent_t ev1 = nullptr);
 int prefill_queries_per_wg(int h);

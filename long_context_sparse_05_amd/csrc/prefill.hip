@@ -11,7 +11,11 @@
 // accumulator rows are whole head sets of its queries: with HP = h rounded
 // up to a power of two (HP <= 16), lane group g of the 32x32 tile holds, in
 // accumulator r, query g*(16/HP) + r/HP and head slot r%HP, so the weighted
-// ReLU head reduction is a register-local sum.  A workgroup (8 waves, two
+// ReLU head reduction is a register-local sum.  Wider head sets (HP = 32:
+// a tile per query; HP = 64: the wave's two tiles per query, e.g. every head
+// of a dense DSA indexer with H_I = 64) give each lane group 16 or 32 of a
+// query's slots, and the two groups' partial sums meet in one lane swap
+// (v_permlane32_swap).  A workgroup (8 waves, two
 // per SIMD) owns QWG consecutive queries, whose A fragments stay in
 // registers, and one split of the key range, which streams through LDS in
 // tiles of 128 keys:
@@ -71,14 +75,18 @@ template <int E> using epi_t = std::integral_constant<int, E>;
 // overflowed) is written at the end.
 template <int HP, int RT, int NW, int KT, bool GEN, bool LISTS>
 __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, int qtile0, int split0) {
-  constexpr int QPT = 32 / HP;                  // queries per 32-row tile
-  constexpr int QPL = 16 / HP;                  // queries per lane (per tile)
-  constexpr int QWG = NW * RT * QPT;            // queries per workgroup
+  constexpr bool WIDE = HP > 16;                // a query's slots span both lane groups
+  constexpr int QPT = WIDE ? 1 : 32 / HP;       // queries per 32-row tile (HP <= 32)
+  constexpr int QPL = WIDE ? 1 : 16 / HP;       // queries per lane (per tile, HP <= 16)
+  constexpr int QPW = RT * 32 / HP;             // queries per wave
+  constexpr int QWG = NW * QPW;                 // queries per workgroup
+  constexpr int LS = WIDE ? (HP == 32 ? 16 : 32) : HP;  // accumulator rows per lane and output
   constexpr int NT = NW * 64;
   constexpr int NB = KT / 32;                   // 32-key column blocks per tile
   constexpr int NDMA = KT / (4 * NW);           // 16-byte DMA loads per thread per tile
   constexpr int TB = KT * 256;                  // bytes per key tile
-  constexpr int OUT = RT * QPL;                 // scores per lane per column block
+  constexpr int OUT = RT * 16 / LS;             // scores per lane per column block (one store each)
+  static_assert(!WIDE || (RT == 2 && (HP == 32 || HP == 64) && !LISTS), "wide head sets");
   // stores per lane per column block that the waits count: the score rows'
   // stores.  List stores are issued only where a lane has a hit and are not
   // counted: with lists every wait is for all outstanding operations.
@@ -113,34 +121,49 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
   bf16x8 qa[RT][8];
   float wv[RT][16];
   char *const wg_rows = (char *)(a.scores + (size_t)qt0 * a.ld);
-  uint32_t rowo[RT][QPL];
-  int lim[RT][QPL];   // position - l32: key kb + l32 is in the prefix iff kb <= lim
-  bool rowok[RT][QPL];
-  float tau[RT][QPL];      // threshold-list cut of the lane's rows (LISTS)
-  uint32_t lcnt[RT][QPL];  // hits of the lane's row so far (the same in the 32 lanes of the row)
-  // The lane's rows: A row l32 of tile rt is (query tA, head slot sA); its
-  // accumulator rows r are (query tile_q0 + g*QPL + r/HP, slot r%HP).  Every
-  // index is clamped so that all loads of a round are issued together (two
-  // dependent rounds: head ids and positions, then query rows and weights).
+  // per output o of the lane (its query out_q(o)): score-row offset, prefix
+  // limit, validity and, with lists, the cut and the hit count
+  uint32_t rowo[OUT];
+  int lim[OUT];       // position - l32: key kb + l32 is in the prefix iff kb <= lim
+  bool rowok[OUT];
+  float tau[OUT];     // threshold-list cut of the lane's rows (LISTS)
+  uint32_t lcnt[OUT]; // hits of the lane's row so far (the same in the 32 lanes of the row)
+  // (query, head slot) of A row (gg, rr) of tile rt -- also of accumulator r
+  // of lane group gg -- and the query of output o.  HP <= 16: tile rt holds
+  // queries tile_q0 + gg*QPL + rr/HP, slot rr%HP; HP = 32: tile rt is query
+  // rt of the wave, slot gg*16 + rr; HP = 64: both tiles are the wave's
+  // query, slot rt*32 + gg*16 + rr.
+  auto row_q = [&](int rt, int gg, int rr) {
+    if constexpr (!WIDE) return qt0 + (wave * RT + rt) * QPT + gg * QPL + rr / HP;
+    else return qt0 + wave * QPW + (HP == 32 ? rt : 0);
+  };
+  auto row_s = [&](int rt, int gg, int rr) {
+    if constexpr (!WIDE) return rr % HP;
+    else return (HP == 64 ? rt * 32 : 0) + gg * 16 + rr;
+  };
+  auto out_q = [&](int o) {
+    if constexpr (!WIDE) return qt0 + (wave * RT + o / QPL) * QPT + g * QPL + o % QPL;
+    else return qt0 + wave * QPW + o;
+  };
+  // head id of slot sl of query t: the routed list, or head sl itself (dense)
+  auto head_of = [&](int t, int sl) { return a.heads ? a.heads[(size_t)t * a.h + sl] : sl; };
+  // Every index is clamped so that all loads of a round are issued together
+  // (two dependent rounds: head ids and positions, then query rows and
+  // weights).
   const int Tm = a.T - 1, hm = a.h - 1;
-  int jq[RT], jw[RT][16], pos[RT][QPL];
+  int jq[RT], jw[RT][16], pos[OUT];
+  const int ag = (l32 >> 2) & 1, ar = ((l32 >> 3) << 2) | (l32 & 3);  // A row l32 = (group, row)
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int tile_q0 = qt0 + (wave * RT + rt) * QPT;
-    const int gg = (l32 >> 2) & 1, rr = ((l32 >> 3) << 2) | (l32 & 3);
-    const int tA = tile_q0 + gg * QPL + rr / HP, sA = rr % HP;
-    jq[rt] = a.heads[(size_t)min(tA, Tm) * a.h + min(sA, hm)];
+    jq[rt] = head_of(min(row_q(rt, ag, ar), Tm), min(row_s(rt, ag, ar), hm));
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      jw[rt][r] = a.heads[(size_t)min(tile_q0 + g * QPL + r / HP, Tm) * a.h + min(r % HP, hm)];
-#pragma unroll
-    for (int qq = 0; qq < QPL; ++qq) pos[rt][qq] = a.q_pos[min(tile_q0 + g * QPL + qq, Tm)];
+    for (int r = 0; r < 16; ++r) jw[rt][r] = head_of(min(row_q(rt, g, r), Tm), min(row_s(rt, g, r), hm));
   }
 #pragma unroll
+  for (int o = 0; o < OUT; ++o) pos[o] = a.q_pos[min(out_q(o), Tm)];
+#pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    const int tile_q0 = qt0 + (wave * RT + rt) * QPT;
-    const int gg = (l32 >> 2) & 1, rr = ((l32 >> 3) << 2) | (l32 & 3);
-    const int tA = tile_q0 + gg * QPL + rr / HP, sA = rr % HP;
+    const int tA = row_q(rt, ag, ar), sA = row_s(rt, ag, ar);
     // (rows past T or past h are zeroed with a mask, not a select: a select
     // of a loaded value may be turned into a branch around the load)
     const uint32_t mA = (tA < a.T && sA < a.h) ? 0xFFFFFFFFu : 0u;
@@ -152,22 +175,25 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int t = tile_q0 + g * QPL + r / HP, slot = r % HP;
+      const int t = row_q(rt, g, r), slot = row_s(rt, g, r);
       const uint32_t wb = __float_as_uint(a.w[(size_t)min(t, Tm) * a.H + jw[rt][r]]);
       wv[rt][r] = __uint_as_float(wb & ((t < a.T && slot < a.h) ? 0xFFFFFFFFu : 0u));
     }
+  }
 #pragma unroll
-    for (int qq = 0; qq < QPL; ++qq) {
-      const int t = tile_q0 + g * QPL + qq;
-      rowo[rt][qq] = (uint32_t)(((t - qt0) * a.ld + l32) * 4);
-      rowok[rt][qq] = t < a.T;
-      lim[rt][qq] = t < a.T ? pos[rt][qq] - l32 : INT_MIN;
-      if constexpr (LISTS) {
-        tau[rt][qq] = a.tau[min(t, Tm)];
-        lcnt[rt][qq] = 0;
-      }
+  for (int o = 0; o < OUT; ++o) {
+    const int t = out_q(o);
+    rowo[o] = (uint32_t)(((t - qt0) * a.ld + l32) * 4);
+    rowok[o] = t < a.T;
+    lim[o] = t < a.T ? pos[o] - l32 : INT_MIN;
+    if constexpr (LISTS) {
+      tau[o] = a.tau[min(t, Tm)];
+      lcnt[o] = 0;
     }
   }
+  // wide head sets: the lane group that stores output o (the other holds
+  // the same sum after the swap)
+  auto stores = [&](int o) { return !WIDE || g == (HP == 32 ? o : 0); };
 
   // Key tiles go straight from global memory into LDS (buffer loads with the
   // LDS-DMA bit): each wave instruction writes 64 consecutive 16-byte slots,
@@ -210,11 +236,9 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
   const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)wg_lists, (short)0, LISTS ? (int)((uint32_t)min(QWG, a.T - qt0) * (uint32_t)a.tcap * 8u) : 0,
       0x00020000);
-  // the first byte of the list of the lane's row (rt, qq): row
-  // (wave RT + rt) QPT + g QPL + qq of the workgroup
+  // the first byte of the list of the lane's output o (row out_q(o) - qt0)
   const uint32_t lrow = LISTS ? (uint32_t)a.tcap * 8u : 0u;
-  const uint32_t lb0 = LISTS ? (uint32_t)((wave * RT * QPT + g * QPL) * a.tcap * 8) : 0u;
-  auto lbase = [&](int rt, int qq) { return lb0 + (uint32_t)(rt * QPT + qq) * lrow; };
+  auto lbase = [&](int o) { return (uint32_t)(out_q(o) - qt0) * lrow; };
   const f32x16 zero = {};
   f32x16 acc[2][RT];
   uint4 bfr[8];
@@ -238,37 +262,42 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
       if (EPI != kEpiNone) {
 #pragma unroll
         for (int v = s * 2 * RT; v < (s + 1) * 2 * RT; ++v) {
-          const int rt = v / 16, r = v % 16, o = v / HP, hs = v % HP;
+          const int rt = v / 16, r = v % 16, o = v / LS, hs = v % LS;
           const float x = __int_as_float(max(__float_as_int(prev[rt][r]), 0));
           sc[o] = hs == 0 ? wv[rt][r] * x : fmaf(wv[rt][r], x, sc[o]);
-          if (hs == HP - 1) {
-            const int ort = o / QPL, oq = o % QPL;
+          if (hs == LS - 1) {
+            if constexpr (WIDE) {  // plus the other lane group's slots of the query
+              const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sc[o]), __float_as_uint(sc[o]),
+                                                               false, false);
+              sc[o] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            }
+            const bool st = stores(o);
             bool in = true;  // the column is in the row's prefix (and in range)
             if (EPI == kEpiFull) {
-              if (!LISTS)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc[o]), srs, rowo[ort][oq], kbp * 4, 0);
+              if (!LISTS && st)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc[o]), srs, rowo[o], kbp * 4, 0);
             } else if (EPI == kEpiCausal) {
-              in = kbp <= lim[ort][oq];
+              in = kbp <= lim[o];
               const float y = in ? sc[o] : -INFINITY;
-              if (!LISTS) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), srs, rowo[ort][oq], kbp * 4, 0);
+              if (!LISTS && st) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(y), srs, rowo[o], kbp * 4, 0);
             } else {
-              in = rowok[ort][oq] && kbp + l32 < k1 && kbp <= lim[ort][oq];
-              if (!LISTS && rowok[ort][oq] && kbp + l32 < k1)
-                *(float *)(wg_rows + (size_t)kbp * 4 + rowo[ort][oq]) = in ? sc[o] : -INFINITY;
+              in = rowok[o] && kbp + l32 < k1 && kbp <= lim[o];
+              if (!LISTS && st && rowok[o] && kbp + l32 < k1)
+                *(float *)(wg_rows + (size_t)kbp * 4 + rowo[o]) = in ? sc[o] : -INFINITY;
             }
             if constexpr (LISTS) {
-              const bool hit = in && sc[o] >= tau[ort][oq];
+              const bool hit = in && sc[o] >= tau[o];
               // the hit's place among its row's hits of this block: lanes
               // 0..31 hold row g = 0, lanes 32..63 row g = 1
               const uint64_t hm = __ballot(hit);
               const uint32_t hlo = (uint32_t)hm, hhi = (uint32_t)(hm >> 32);
               const uint32_t below =
                   __builtin_amdgcn_mbcnt_hi(hhi, __builtin_amdgcn_mbcnt_lo(hlo, 0u)) - (g ? (uint32_t)__popc(hlo) : 0u);
-              const uint32_t slot = lcnt[ort][oq] + below;
-              lcnt[ort][oq] += g ? (uint32_t)__popc(hhi) : (uint32_t)__popc(hlo);
+              const uint32_t slot = lcnt[o] + below;
+              lcnt[o] += g ? (uint32_t)__popc(hhi) : (uint32_t)__popc(hlo);
               if (hit && slot < (uint32_t)a.tcap) {
                 const u32x2 ent = {__float_as_uint(sc[o]), (uint32_t)(kbp + l32)};
-                const uint32_t off = lbase(ort, oq) + slot * 8u;
+                const uint32_t off = lbase(o) + slot * 8u;
                 if (EPI == kEpiGeneric)
                   *(u32x2 *)((char *)wg_lists + off) = ent;
                 else
@@ -346,12 +375,10 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
   }
   if constexpr (LISTS) {  // the rows' hit counts: [split][T]
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int qq = 0; qq < QPL; ++qq) {
-        const int t = qt0 + (wave * RT + rt) * QPT + g * QPL + qq;
-        if (l32 == 0 && t < a.T) a.tcount[(size_t)split_id * a.T + t] = lcnt[rt][qq];
-      }
+    for (int o = 0; o < OUT; ++o) {
+      const int t = out_q(o);
+      if (l32 == 0 && t < a.T) a.tcount[(size_t)split_id * a.T + t] = lcnt[o];
+    }
   }
   if (LISTS) return;  // no score rows
   // columns of this split past every query of the workgroup
@@ -369,7 +396,7 @@ constexpr int pf_rt(int hp) { return hp >= 4 ? 2 : 1; }
 template <int HP, bool LISTS>
 static hipError_t launch_hp(const PrefillArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   constexpr int RT = pf_rt(HP);
-  constexpr int QWG = kPfWaves * RT * (32 / HP);
+  constexpr int QWG = kPfWaves * RT * 32 / HP;
   if (a.split % kPfKeys) return hipErrorInvalidValue;
   if ((uint64_t)QWG * a.ld * 4 > 0x7FFFFFFFull) return hipErrorInvalidValue;
   if ((uint64_t)a.Lmax * 256 > 0x7FFFFFFFull) return hipErrorInvalidValue;
@@ -402,13 +429,13 @@ static hipError_t launch_hp(const PrefillArgs &a, hipStream_t st, hipEvent_t ev0
 }
 
 int prefill_queries_per_wg(int h) {
-  const int hp = h <= 1 ? 1 : h <= 2 ? 2 : h <= 4 ? 4 : h <= 8 ? 8 : 16;
-  return kPfWaves * pf_rt(hp) * (32 / hp);
+  const int hp = h <= 1 ? 1 : h <= 2 ? 2 : h <= 4 ? 4 : h <= 8 ? 8 : h <= 16 ? 16 : h <= 32 ? 32 : 64;
+  return kPfWaves * pf_rt(hp) * 32 / hp;
 }
 
 bool prefill_supported(int h, int ld, int Lmax) {
-  return h >= 1 && h <= 16 && ld >= Lmax && (uint64_t)prefill_queries_per_wg(h) * ld * 4 <= 0x7FFFFFFFull &&
-         (uint64_t)Lmax * 256 <= 0x7FFFFFFFull;
+  return h >= 1 && h <= kPrefillMaxHeads && ld >= Lmax &&
+         (uint64_t)prefill_queries_per_wg(h) * ld * 4 <= 0x7FFFFFFFull && (uint64_t)Lmax * 256 <= 0x7FFFFFFFull;
 }
 
 // The threshold lists cost two registers per (lane, row): the tilings with
@@ -425,6 +452,10 @@ static hipError_t launch_lists(const PrefillArgs &a, hipStream_t st, hipEvent_t 
   }
   if (a.h >= 5 && a.h <= 8) return launch_hp<8, LISTS>(a, st, ev0, ev1);
   if (a.h >= 9 && a.h <= 16) return launch_hp<16, LISTS>(a, st, ev0, ev1);
+  if constexpr (!LISTS) {
+    if (a.h <= 32) return launch_hp<32, false>(a, st, ev0, ev1);
+    if (a.h <= 64) return launch_hp<64, false>(a, st, ev0, ev1);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -797,6 +797,11 @@ PREFILL_CASES = [
     # ragged only in the keys, or only in the queries
     (3000, 128, 32, 8, "tail"),
     (2048, 100, 32, 4, "tail"),
+    # wide head sets: a tile per query (h <= 32) or two (h <= 64)
+    (3000, 100, 64, 24, "random"),
+    (2100, 80, 32, 32, "tail"),
+    (2600, 72, 64, 40, "tail"),
+    (2048, 64, 64, 64, "random"),
 ]
 
 
@@ -841,6 +846,38 @@ def test_prefill_scores_and_selection(Lmax, T, H, h, positions):
     fh, fi, fv = abi.indexer(b, pooled, B, h, k)
     assert np.array_equal(np_(fh), np_(rh))
     assert [set(r) for r in np_(fi)] == [set(r) for r in np_(ri)]
+
+
+DENSE_PREFILL_CASES = [
+    # Lmax, T, H, positions
+    (3000, 200, 32, "tail"),
+    (2500, 130, 64, "random"),
+    (4096, 128, 64, "tail"),   # whole query and key tiles
+    (1800, 96, 16, "tail"),
+    (2200, 70, 48, "random"),
+]
+
+
+@pytest.mark.parametrize("Lmax,T,H,positions", DENSE_PREFILL_CASES)
+def test_prefill_dense_all_heads(Lmax, T, H, positions):
+    """The dense indexer (every head, no routing) on a prefill chunk takes
+    the MFMA tiling too (up to 64 heads a query): scores and selections
+    match the oracle's DSA indexer."""
+    abi = _abi()
+    case = make_prefill(Lmax, T, H, 23, positions)
+    b = upload(case)
+    ob = orc.Batch.from_case(case)
+    got = np_(abi.score(b, None))
+    osc = orc.scores(ob)
+    parity.check_scores(got, osc, n_valid(case))
+    k = min(300, Lmax)
+    idx, val = abi.indexer_dense(b, k)
+    idx, val = np_(idx), np_(val)
+    for t in range(T):
+        n = int(n_valid(case)[t])
+        parity.check_exact_topk(idx[t], val[t], got[t], n, k, orc.topk_f32)
+        oidx = orc.topk(osc[t, :n], k)[0]
+        parity.check_set(idx[t], oidx, lambda i: osc[t, i], n, k, parity.row_sbar(osc[t], n))
 
 
 def test_prefill_integer_inputs_bit_exact():
