@@ -384,6 +384,46 @@ int prefill_select(const misa_batch *b, const int32_t *heads, int h, int k, int3
   return hip_status(launch_topk_rowselect(t, st));
 }
 
+// Several query rows per sequence (S > 1, at least two rows per sequence on
+// average, up to 64 head slots): the MFMA tiling over a tile table built on
+// the device, so that the rows of a sequence share one pass over its keys.
+// Rows of one sequence must be contiguous for this to pay; when they are not
+// (more tiles than the bound), every row is scored on its own instead.
+bool use_grouped(const misa_batch *b, const int32_t *heads, int h) {
+  const int nh = heads ? h : b->H;
+  return b->S > 1 && b->T >= 2 * b->S && prefill_supported(nh, b->Lmax, b->Lmax);
+}
+size_t grouped_bytes(const misa_batch *b) {
+  return b->S > 1 ? align_up((size_t)b->T * sizeof(int2)) + kAlign : 0;
+}
+
+// The grouped scoring into sc [T][Lmax] (gws: grouped_bytes of workspace).
+int grouped_score(const misa_batch *b, const int32_t *heads, int h, float *sc, void *gws, hipStream_t st,
+                  void *ev_start = nullptr, void *ev_stop = nullptr) {
+  const int nh = heads ? h : b->H;
+  const int qwg = prefill_queries_per_wg(nh);
+  const int bound = std::min(b->T, (b->T + qwg - 1) / qwg + b->S);
+  int2 *tiles = (int2 *)gws;
+  uint32_t *cnt = (uint32_t *)((char *)gws + align_up((size_t)b->T * sizeof(int2)));
+  if (launch_prefill_tiles(b->q_seq, b->T, nh, bound, tiles, cnt, cnt + 1, st) != hipSuccess) return MISA_ERR_HIP;
+  PrefillArgs p = make_prefill_args(b, heads, h, sc);
+  p.q_seq = b->q_seq;
+  p.tiles = tiles;
+  p.ntiles = cnt;
+  p.ntile_bound = bound;
+  p.split = prefill_split(bound * qwg, nh, b->Lmax);
+  if (launch_score_prefill(p, st, (hipEvent_t)ev_start, (hipEvent_t)ev_stop) != hipSuccess) return MISA_ERR_HIP;
+  // rows not contiguous by sequence: each row on its own (cnt[1] = T), else nothing
+  ScoreArgs s = make_score_args(b, heads, nh);
+  s.scores = sc;
+  s.cand = nullptr;
+  s.ncols = b->Lmax;
+  s.ld = b->Lmax;
+  s.chunk = score_chunk(b->T, b->Lmax);
+  s.rowcount = cnt + 1;
+  return hip_status(launch_score_rows(s, st));
+}
+
 
 }  // namespace
 
@@ -417,7 +457,7 @@ int misa_workspace_bytes(const misa_batch *b, int32_t op, int32_t B, int32_t h, 
     case MISA_OP_SCORE_TOPK:
       if (k < 1 || k > b->Lmax) return MISA_ERR_SHAPE;
       *bytes = select_layout(b->T, b->Lmax, k, true).total +
-               (op == MISA_OP_SCORE_TOPK ? tlist_layout(b, h, k).total : 0);
+               (op == MISA_OP_SCORE_TOPK ? tlist_layout(b, h, k).total : 0) + grouped_bytes(b);
       return MISA_OK;
     case MISA_OP_RERANK:
       if (k < 1 || kc < k || kc > b->Lmax) return MISA_ERR_SHAPE;
@@ -425,7 +465,8 @@ int misa_workspace_bytes(const misa_batch *b, int32_t op, int32_t B, int32_t h, 
       return MISA_OK;
     case MISA_OP_INDEXER:
       if (B < 1 || B > b->Lmax || h < 1 || h > b->H || k < 1 || k > b->Lmax) return MISA_ERR_SHAPE;
-      *bytes = route_bytes(b, B) + select_layout(b->T, b->Lmax, k, true).total + tlist_layout(b, h, k).total;
+      *bytes = route_bytes(b, B) + select_layout(b->T, b->Lmax, k, true).total + tlist_layout(b, h, k).total +
+               grouped_bytes(b);
       return MISA_OK;
     case MISA_OP_TOPK:
       if (k < 1) return MISA_ERR_SHAPE;
@@ -553,9 +594,15 @@ int misa_score_topk_ev(const misa_batch *b, const int32_t *heads, int32_t h, int
   if (k < 1 || k > b->Lmax) return MISA_ERR_SHAPE;
   const SelectLayout L = select_layout(b->T, b->Lmax, k, true);
   const TlistLayout TL = heads ? tlist_layout(b, h, k) : TlistLayout{};
-  if (ws_bytes < L.total + TL.total) return MISA_ERR_WORKSPACE;
+  if (ws_bytes < L.total + TL.total + grouped_bytes(b)) return MISA_ERR_WORKSPACE;
   if (use_prefill(b, heads, h))
     return prefill_select(b, heads, h, k, idx, val, ws, L, TL, (hipStream_t)stream, ev_start, ev_stop);
+  if (use_grouped(b, heads, h)) {
+    float *sc = (float *)((char *)ws + L.scores);
+    rc = grouped_score(b, heads, h, sc, (char *)ws + L.total + TL.total, (hipStream_t)stream, ev_start, ev_stop);
+    if (rc) return rc;
+    return run_select(nullptr, sc, b->T, b->Lmax, b->q_pos, 1, nullptr, k, idx, val, ws, L, (hipStream_t)stream);
+  }
   ScoreArgs s = make_score_args(b, heads, heads ? h : b->H);
   s.scores = (float *)((char *)ws + L.scores);
   s.cand = nullptr;
@@ -603,20 +650,28 @@ int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t
   const size_t rbytes = route_bytes(b, B);
   const SelectLayout L = select_layout(b->T, b->Lmax, k, true);
   const TlistLayout TL = tlist_layout(b, h, k);
-  if (ws_bytes < rbytes + L.total + TL.total) return MISA_ERR_WORKSPACE;
+  if (ws_bytes < rbytes + L.total + TL.total + grouped_bytes(b)) return MISA_ERR_WORKSPACE;
   void *sws = (char *)ws + rbytes;
   const RouteArgs ra = make_route_args(b, pooled, B, h, mode, heads, head_score, ws);
   // many queries of one sequence: the tiled router writes the heads; the
-  // prefill tiling reads them from memory; otherwise the router kernel
-  // leaves partial sums that the scoring kernel's prologue reduces and ranks
+  // prefill and grouped tilings read them from memory; otherwise the router
+  // kernel leaves partial sums that the scoring kernel's prologue reduces
+  // and ranks
   const bool tiled_router = route_tiled(b), prefill = use_prefill(b, heads, h);
-  const bool in_prologue = !tiled_router && !prefill;
-  hipError_t re = tiled_router ? launch_route_tile(ra, (hipStream_t)stream)
-                  : prefill    ? launch_route(ra, (hipStream_t)stream)
-                               : launch_route_partial(ra, (hipStream_t)stream);
+  const bool grouped = !prefill && use_grouped(b, heads, h);
+  const bool in_prologue = !tiled_router && !prefill && !grouped;
+  hipError_t re = tiled_router          ? launch_route_tile(ra, (hipStream_t)stream)
+                  : (prefill || grouped) ? launch_route(ra, (hipStream_t)stream)
+                                         : launch_route_partial(ra, (hipStream_t)stream);
   if (re != hipSuccess) return MISA_ERR_HIP;
   if (prefill)
     return prefill_select(b, heads, h, k, idx, val, sws, L, TL, (hipStream_t)stream, ev_start, ev_stop);
+  if (grouped) {
+    float *sc = (float *)((char *)sws + L.scores);
+    rc = grouped_score(b, heads, h, sc, (char *)sws + L.total + TL.total, (hipStream_t)stream, ev_start, ev_stop);
+    if (rc) return rc;
+    return run_select(nullptr, sc, b->T, b->Lmax, b->q_pos, 1, nullptr, k, idx, val, sws, L, (hipStream_t)stream);
+  }
   ScoreArgs s = make_score_args(b, heads, h);
   if (in_prologue) {  // heads come from the router's partial sums
     s.heads = nullptr;

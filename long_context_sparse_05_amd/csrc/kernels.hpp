@@ -38,8 +38,9 @@ struct ScoreArgs {
   int nparts, mode;
   int32_t *heads_out;
   float *g_out;
-  // A row list (optional; direct rows, nh <= 16): the rows rowlist[0 ..
-  // *rowcount) are scored instead of rows 0 .. T-1 (T bounds the count).
+  // A row count (optional; direct rows, nh <= 64): the rows rowlist[0 ..
+  // *rowcount) -- rows 0 .. *rowcount-1 when rowlist is nullptr -- are
+  // scored instead of rows 0 .. T-1 (T bounds the count).
   const int32_t *rowlist;
   const uint32_t *rowcount;
   int nh, H, Lmax, T;
@@ -73,7 +74,22 @@ struct PrefillArgs {
   uint2 *tlists;
   uint32_t *tcount;
   int tcap;
+  // Several sequences (optional, tiles != nullptr): workgroup row y takes
+  // tile y of the table -- (first row, sequence), the rows from there on
+  // with that q_seq, at most the tiling's queries per workgroup -- if y <
+  // *ntiles; the grid has ntile_bound rows.  seq is then unused.
+  const int32_t *q_seq;
+  const int2 *tiles;
+  const uint32_t *ntiles;
+  int ntile_bound;
 };
+// The tile table of a batch of several sequences (prefill.hip): runs of
+// equal q_seq cut into tiles of prefill_queries_per_wg(h) rows.  When the
+// rows of a sequence are not contiguous and the tiles would pass `bound`,
+// *ntiles = 0 and *fallback = T (the per-row scoring then takes every row);
+// else *fallback = 0.
+hipError_t launch_prefill_tiles(const int32_t *q_seq, int T, int h, int bound, int2 *tiles, uint32_t *ntiles,
+                                uint32_t *fallback, hipStream_t st);
 // key tile of the prefill kernel: PrefillArgs::split must be a multiple
 constexpr int kPrefillKeyTile = 128;
 constexpr int kPrefillMaxHeads = 64;  // head slots per query the tiling takes

@@ -44,6 +44,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace misa {
 
@@ -99,23 +100,41 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  const int qt0 = (blockIdx.y + qtile0) * QWG;
+  // the workgroup's query rows: QWG consecutive rows from qt0 of sequence
+  // a.seq, or with a tile table the rows of tile blockIdx.y's sequence
+  int qt0 = (blockIdx.y + qtile0) * QWG, seq = a.seq;
+  if (a.tiles) {  // uniform
+    if (blockIdx.y >= *a.ntiles) return;
+    const int2 tl = a.tiles[blockIdx.y];
+    qt0 = tl.x;
+    seq = tl.y;
+  }
   const int k0 = (blockIdx.x + split0) * a.split;
   const int k1 = min(k0 + a.split, a.Lmax);
 
+  __shared__ uint8_t sh_in[QWG];  // row qt0 + i belongs to the workgroup
+  __shared__ int sh_nin;
   if (tid == 0) {
     sh_pmax = -1;
     sh_pmin = 0x7FFFFFFF;
+    sh_nin = 0;
   }
   __syncthreads();
-  if (tid < QWG && qt0 + tid < a.T) {
-    const int p = a.q_pos[qt0 + tid];
-    atomicMax(&sh_pmax, p);
-    atomicMin(&sh_pmin, p);
+  if (tid < QWG) {
+    const int t = qt0 + tid;
+    const bool in = t < a.T && (!a.tiles || a.q_seq[t] == seq);
+    sh_in[tid] = in;
+    if (in) {
+      const int p = a.q_pos[t];
+      atomicMax(&sh_pmax, p);
+      atomicMin(&sh_pmin, p);
+      atomicAdd(&sh_nin, 1);
+    }
   }
   __syncthreads();
+  auto row_in = [&](int t) { return sh_in[t - qt0] != 0; };  // t in [qt0, qt0 + QWG)
   const int kend = __builtin_amdgcn_readfirstlane(min(k1, sh_pmax + 1));
-  const bool all_rows = qt0 + QWG <= a.T;
+  const bool all_rows = sh_nin == QWG;
   const int kfull = __builtin_amdgcn_readfirstlane(all_rows ? min(k1, sh_pmin + 1) : 0);
 
   bf16x8 qa[RT][8];
@@ -166,7 +185,7 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
     const int tA = row_q(rt, ag, ar), sA = row_s(rt, ag, ar);
     // (rows past T or past h are zeroed with a mask, not a select: a select
     // of a loaded value may be turned into a branch around the load)
-    const uint32_t mA = (tA < a.T && sA < a.h) ? 0xFFFFFFFFu : 0u;
+    const uint32_t mA = (row_in(tA) && sA < a.h) ? 0xFFFFFFFFu : 0u;
     const uint16_t *qrow = a.q + ((size_t)min(tA, Tm) * a.H + jq[rt]) * kD + g * 8;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -177,15 +196,15 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
     for (int r = 0; r < 16; ++r) {
       const int t = row_q(rt, g, r), slot = row_s(rt, g, r);
       const uint32_t wb = __float_as_uint(a.w[(size_t)min(t, Tm) * a.H + jw[rt][r]]);
-      wv[rt][r] = __uint_as_float(wb & ((t < a.T && slot < a.h) ? 0xFFFFFFFFu : 0u));
+      wv[rt][r] = __uint_as_float(wb & ((row_in(t) && slot < a.h) ? 0xFFFFFFFFu : 0u));
     }
   }
 #pragma unroll
   for (int o = 0; o < OUT; ++o) {
     const int t = out_q(o);
     rowo[o] = (uint32_t)(((t - qt0) * a.ld + l32) * 4);
-    rowok[o] = t < a.T;
-    lim[o] = t < a.T ? pos[o] - l32 : INT_MIN;
+    rowok[o] = row_in(t);
+    lim[o] = rowok[o] ? pos[o] - l32 : INT_MIN;
     if constexpr (LISTS) {
       tau[o] = a.tau[min(t, Tm)];
       lcnt[o] = 0;
@@ -203,7 +222,7 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
   // past it read as zero (their scores are masked).
   const int rr = 4 * wave + (lane >> 4);
   const uint32_t dvoff = (uint32_t)(rr * 256 + (((lane & 15) ^ (rr & 15)) * 16));
-  const char *kseq = (const char *)(a.keys + (size_t)a.seq * a.Lmax * kD);
+  const char *kseq = (const char *)(a.keys + (size_t)seq * a.Lmax * kD);
   auto buf_of = [&](auto b) -> char * {
     if constexpr (decltype(b)::value == 0) return (char *)ktile0; else return (char *)ktile1;
   };
@@ -384,8 +403,8 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
   // columns of this split past every query of the workgroup
   const int cstart = min(k1, k0 + ntile * KT);
   for (int qi = 0; qi < QWG; ++qi) {
+    if (!sh_in[qi]) continue;  // uniform
     const int t = qt0 + qi;
-    if (t >= a.T) break;
     for (int c = cstart + tid; c < k1; c += NT) a.scores[(size_t)t * a.ld + c] = -INFINITY;
   }
 }
@@ -416,6 +435,17 @@ static hipError_t launch_hp(const PrefillArgs &a, hipStream_t st, hipEvent_t ev0
     else
       hipLaunchKernelGGL(kernel, grid, dim3(kPfWaves * 64), 0, st, a, qtile0, split0);
   };
+  if (a.tiles) {  // a tile table: every workgroup checked (ragged tiles and splits)
+    if (LISTS || !a.ntiles || !a.q_seq || a.ntile_bound < 1 || a.ntile_bound > 65535) return hipErrorInvalidValue;
+    const dim3 grid(nsplit, a.ntile_bound);
+    if (ev0 || ev1)
+      hipExtLaunchKernelGGL((score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, true, false>), grid,
+                            dim3(kPfWaves * 64), 0, st, ev0, ev1, 0, a, 0, 0);
+    else
+      hipLaunchKernelGGL((score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, true, false>), grid, dim3(kPfWaves * 64),
+                         0, st, a, 0, 0);
+    return hipGetLastError();
+  }
   if (l0) launch(0, score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, false, LISTS>, dim3(ns_full, nq_full), 0, 0);
   if (l1)  // the ragged last row of query tiles, all splits
     launch(1, score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, true, LISTS>, dim3(nsplit, 1), nq_full, 0);
@@ -465,6 +495,53 @@ hipError_t launch_score_prefill(const PrefillArgs &a, hipStream_t st, hipEvent_t
       (uint64_t)prefill_queries_per_wg(a.h) * a.tcap * 8 > 0x7FFFFFF0ull)
     return hipErrorInvalidValue;
   return launch_lists<true>(a, st, ev0, ev1);
+}
+
+// One workgroup walks the rows 1024 at a time: a run starts where q_seq
+// changes; the run start of every row is a running maximum (a scan in LDS);
+// a tile starts at every run start and every qwg rows after it; tile slots
+// come from a block scan of those starts.
+__global__ __launch_bounds__(1024) void prefill_tiles_kernel(const int32_t *q_seq, int T, int qwg, int bound,
+                                                             int2 *tiles, uint32_t *ntiles, uint32_t *fallback) {
+  constexpr int NT = 1024;
+  __shared__ int smax[NT];
+  __shared__ uint32_t sh[NT / kWave + 4];
+  const int tid = threadIdx.x;
+  int carry_rs = 0;
+  uint32_t carry_n = 0;
+  for (int base = 0; base < T; base += NT) {
+    const int t = base + tid;
+    const int q = t < T ? q_seq[t] : 0;
+    smax[tid] = (t < T && (t == 0 || q != q_seq[t - 1])) ? t : -1;
+    __syncthreads();
+    for (int off = 1; off < NT; off <<= 1) {
+      const int v = tid >= off ? smax[tid - off] : -1;
+      __syncthreads();
+      smax[tid] = max(smax[tid], v);
+      __syncthreads();
+    }
+    const int rs = max(smax[tid], carry_rs);  // the row's run start
+    const uint32_t ts = (t < T && (t - rs) % qwg == 0) ? 1u : 0u;
+    uint32_t total;
+    const uint32_t pos = carry_n + block_scan<NT>(ts, sh, total) - ts;
+    if (ts && pos < (uint32_t)bound) tiles[pos] = make_int2(t, q);
+    carry_rs = max(carry_rs, smax[NT - 1]);
+    carry_n += total;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const bool fits = carry_n <= (uint32_t)bound;
+    *ntiles = fits ? carry_n : 0u;
+    *fallback = fits ? 0u : (uint32_t)T;
+  }
+}
+
+hipError_t launch_prefill_tiles(const int32_t *q_seq, int T, int h, int bound, int2 *tiles, uint32_t *ntiles,
+                                uint32_t *fallback, hipStream_t st) {
+  if (T < 1 || bound < 1 || !prefill_supported(h, 1, 1)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prefill_tiles_kernel, dim3(1), dim3(1024), 0, st, q_seq, T, prefill_queries_per_wg(h), bound,
+                     tiles, ntiles, fallback);
+  return hipGetLastError();
 }
 
 }  // namespace misa

@@ -264,14 +264,15 @@ __device__ __forceinline__ void score_row_chunk(const ScoreArgs &a, const int t)
 }
 
 // Grid (chunks, rows): workgroup (x, y) scores chunk x of row y -- or, with
-// a row list (RLIST), of rows rowlist[y], rowlist[y + gridDim.y], ... below
-// *rowcount, one after another.
+// a row count (RLIST), of rows rowlist[y], rowlist[y + gridDim.y], ...
+// (rows y, y + gridDim.y, ... without a list) below *rowcount, one after
+// another.
 template <int HT, bool GATHER, bool ROUTE, int U, int NW, bool RLIST>
 __global__ __launch_bounds__(NW * 64) void score_rows_kernel(ScoreArgs a) {
   if constexpr (RLIST) {
     const uint32_t nrows = *a.rowcount;
     for (uint32_t y = blockIdx.y; y < nrows; y += gridDim.y) {
-      score_row_chunk<HT, GATHER, ROUTE, U, NW>(a, a.rowlist[y]);
+      score_row_chunk<HT, GATHER, ROUTE, U, NW>(a, a.rowlist ? a.rowlist[y] : (int)y);
       __syncthreads();  // the next row reuses the shared memory
     }
   } else {
@@ -284,8 +285,8 @@ constexpr int kRowListGrid = 64;
 
 template <int HT, bool GATHER, bool ROUTE>
 static hipError_t launch_ht(const ScoreArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-  if (a.rowlist) {  // (at most 16 heads: the rows a prefill chunk's select rescores)
-    if constexpr (HT == 1 && !GATHER && !ROUTE) {
+  if (a.rowcount) {  // (at most 64 heads: rows a prefill or grouped call hands back)
+    if constexpr (HT <= 4 && !GATHER && !ROUTE) {
       if (!a.rowcount || ev0 || ev1 || a.chunk > kMaxScoreChunk) return hipErrorInvalidValue;
       constexpr int U = 2, NW = score_waves<HT, false>();
       const dim3 grid((a.ncols + a.chunk - 1) / a.chunk, a.T < kRowListGrid ? a.T : kRowListGrid);
