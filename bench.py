@@ -120,7 +120,9 @@ def summarize_counters(workload, fetch_dir, write_dir, cfetch_dir, cwrite_dir):
     WRITE_SIZE, each scaled by the same counter on the plain copy of known
     size) to profiles/score_kernel_traffic.json, keyed by the kernel-source
     hash so a changed kernel reads as unmeasured."""
-    kname = "score_rows_kernel"
+    # the fused call's scoring kernel (router reduce in its prologue), the one
+    # the headline's roofline times -- not the separate-call or dense variants
+    kname = "score_rows_kernel<1, false, true,"
     f_k = _per_kernel_kib(_counter_rows(fetch_dir), "FETCH_SIZE", kname)
     w_k = _per_kernel_kib(_counter_rows(write_dir), "WRITE_SIZE", kname)
     # the runtime's device copy kernel moves the known bytes (torch's fill of
@@ -329,6 +331,23 @@ def measure(workload, K, W, ev, cpu=True, cpu_rows_cap=None):
     # cold caches: before each step a 1 GiB fill evicts L2 and the 256 MB
     # MALL, and events bracket the step alone (reported beside the headline,
     # which times back-to-back steps)
+    # context only: the dense DSA indexer (every head, no routing) on the same
+    # inputs and k, warm back-to-back steps like the headline
+    dsa_us = None
+    if routed and not hier and kind != "dagger":
+        ws_dd = b.workspace(abi.MISA_OP_DENSE, k=k)
+        di = torch.empty((b.T, k), dtype=torch.int32, device=dev)
+        dv = torch.empty((b.T, k), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            abi.score_topk(b, None, k, idx=di, val=dv, ws=ws_dd)
+        nd = max(2, min(K, 5))
+        ev.record(t_start, sp)
+        for _ in range(nd):
+            abi.score_topk(b, None, k, idx=di, val=dv, ws=ws_dd)
+        ev.record(t_stop, sp)
+        torch.cuda.synchronize()
+        dsa_us = ev.ms(t_start, t_stop) / nd * 1e3
+        del ws_dd, di, dv
     flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     cev = [(ev.create(), ev.create()) for _ in range(K)]
     for i in range(K):
@@ -389,6 +408,11 @@ def measure(workload, K, W, ev, cpu=True, cpu_rows_cap=None):
         res["config"]["kept_blocks"] = m
     if ms_sep is not None:
         res["us_per_batch_separate_calls"] = ms_sep * 1e3
+    if dsa_us is not None:
+        res["dsa_vs_misa"] = {"dsa_dense_us_per_step": dsa_us, "misa_us_per_step": ms_step * 1e3,
+                              "dsa_over_misa": dsa_us / (ms_step * 1e3),
+                              "note": "context, not a target: the dense indexer over all %d heads "
+                                      "on the same inputs and k" % b.H}
     if pool_us is not None:
         res["pool_us_once_per_cache"] = pool_us
     if kind != "prefill" and not hier:
