@@ -331,6 +331,19 @@ def measure(workload, K, W, ev, cpu=True, cpu_rows_cap=None):
     # cold caches: before each step a 1 GiB fill evicts L2 and the 256 MB
     # MALL, and events bracket the step alone (reported beside the headline,
     # which times back-to-back steps)
+    # context for several queries per sequence: the same routed rows scored
+    # one by one (misa_score, which takes the per-row kernel), kernel time
+    per_row_us = None
+    if routed and cfg.get("queries_per_seq", 1) > 1 and b.S > 1:
+        sc_rows = torch.empty((b.T, b.Lmax), dtype=torch.float32, device=dev)
+        abi.score(b, heads, out=sc_rows)
+        ev.record(t_start, sp)
+        for _ in range(5):
+            abi.score(b, heads, out=sc_rows)
+        ev.record(t_stop, sp)
+        torch.cuda.synchronize()
+        per_row_us = ev.ms(t_start, t_stop) / 5 * 1e3
+        del sc_rows
     # context only: the dense DSA indexer (every head, no routing) on the same
     # inputs and k, warm back-to-back steps like the headline
     dsa_us = None
@@ -382,6 +395,17 @@ def measure(workload, K, W, ev, cpu=True, cpu_rows_cap=None):
                 "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                 "kernel": "score_rows_kernel (gathered candidate rows, %d heads)" % nh,
                 "alg_bytes_per_launch": alg_bytes}
+    elif cfg.get("queries_per_seq", 1) > 1 and b.S > 1:
+        # several queries per sequence: each sequence's keys are read once for
+        # all its rows (its longest prefix), plus the routed query rows
+        qp = case["q_pos"].astype(np.int64)
+        seq_keys = sum(int(qp[case["q_seq"] == s_].max()) + 1 for s_ in range(b.S))
+        alg_bytes = seq_keys * KEY_BYTES + b.T * nh * KEY_BYTES
+        achieved = alg_bytes / (score_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "kernel": "score_prefill_kernel (multi-query tile table, %d routed heads)" % nh,
+                "alg_bytes_per_launch": alg_bytes}
     else:
         alg_bytes = n_keys * KEY_BYTES + b.T * nh * KEY_BYTES  # keys streamed + query rows
         achieved = alg_bytes / (score_ms * 1e-3) / 1e9
@@ -408,6 +432,10 @@ def measure(workload, K, W, ev, cpu=True, cpu_rows_cap=None):
         res["config"]["kept_blocks"] = m
     if ms_sep is not None:
         res["us_per_batch_separate_calls"] = ms_sep * 1e3
+    if per_row_us is not None:
+        res["multi_query"] = {"shared_pass_scoring_us": score_ms * 1e3, "per_row_scoring_us": per_row_us,
+                              "note": "the routed rows scored with a shared pass over each sequence's keys "
+                                      "(the step) against one pass per row (misa_score)"}
     if dsa_us is not None:
         res["dsa_vs_misa"] = {"dsa_dense_us_per_step": dsa_us, "misa_us_per_step": ms_step * 1e3,
                               "dsa_over_misa": dsa_us / (ms_step * 1e3),

@@ -401,7 +401,7 @@ size_t grouped_bytes(const misa_batch *b) {
 int grouped_score(const misa_batch *b, const int32_t *heads, int h, float *sc, void *gws, hipStream_t st,
                   void *ev_start = nullptr, void *ev_stop = nullptr) {
   const int nh = heads ? h : b->H;
-  const int qwg = prefill_queries_per_wg(nh);
+  const int qwg = prefill_group_queries_per_wg(nh);
   const int bound = std::min(b->T, (b->T + qwg - 1) / qwg + b->S);
   int2 *tiles = (int2 *)gws;
   uint32_t *cnt = (uint32_t *)((char *)gws + align_up((size_t)b->T * sizeof(int2)));
@@ -411,7 +411,11 @@ int grouped_score(const misa_batch *b, const int32_t *heads, int h, float *sc, v
   p.tiles = tiles;
   p.ntiles = cnt;
   p.ntile_bound = bound;
-  p.split = prefill_split(bound * qwg, nh, b->Lmax);
+  // about two four-wave workgroups per compute unit over the tiles, at
+  // least 512 keys a split
+  const int nsplit = std::max(1, std::min((b->Lmax + 511) / 512, (512 + bound / 2) / bound));
+  const int split = (b->Lmax + nsplit - 1) / nsplit;
+  p.split = (split + kPrefillKeyTile - 1) / kPrefillKeyTile * kPrefillKeyTile;
   if (launch_score_prefill(p, st, (hipEvent_t)ev_start, (hipEvent_t)ev_stop) != hipSuccess) return MISA_ERR_HIP;
   // rows not contiguous by sequence: each row on its own (cnt[1] = T), else nothing
   ScoreArgs s = make_score_args(b, heads, nh);

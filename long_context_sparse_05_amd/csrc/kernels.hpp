@@ -84,7 +84,7 @@ struct PrefillArgs {
   int ntile_bound;
 };
 // The tile table of a batch of several sequences (prefill.hip): runs of
-// equal q_seq cut into tiles of prefill_queries_per_wg(h) rows.  When the
+// equal q_seq cut into tiles of prefill_group_queries_per_wg(h) rows.  When the
 // rows of a sequence are not contiguous and the tiles would pass `bound`,
 // *ntiles = 0 and *fallback = T (the per-row scoring then takes every row);
 // else *fallback = 0.
@@ -96,6 +96,7 @@ constexpr int kPrefillMaxHeads = 64;  // head slots per query the tiling takes
 hipError_t launch_score_prefill(const PrefillArgs &a, hipStream_t st, hipEvent_t ev0 = nullptr,
                                 hipEvent_t ev1 = nullptr);
 int prefill_queries_per_wg(int h);
+int prefill_group_queries_per_wg(int h);  // with a tile table
 bool prefill_supported(int h, int ld, int Lmax);  // the launch shape fits h, the row length and the keys
 bool prefill_lists_supported(int h);              // the tiling for h heads can write threshold lists
 

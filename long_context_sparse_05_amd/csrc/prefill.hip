@@ -411,6 +411,11 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
 
 constexpr int kPfWaves = 8, kPfKeys = kPrefillKeyTile;
 constexpr int pf_rt(int hp) { return hp >= 4 ? 2 : 1; }
+// A tile table (several sequences, a handful of queries each): four waves
+// and one A tile per wave (two for wide head sets), so a tile of a short run
+// of queries carries less padding through the MFMAs.
+constexpr int kPfGroupWaves = 4;
+constexpr int pf_group_rt(int hp) { return hp > 16 ? 2 : 1; }
 
 template <int HP, bool LISTS>
 static hipError_t launch_hp(const PrefillArgs &a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
@@ -437,13 +442,14 @@ static hipError_t launch_hp(const PrefillArgs &a, hipStream_t st, hipEvent_t ev0
   };
   if (a.tiles) {  // a tile table: every workgroup checked (ragged tiles and splits)
     if (LISTS || !a.ntiles || !a.q_seq || a.ntile_bound < 1 || a.ntile_bound > 65535) return hipErrorInvalidValue;
-    const dim3 grid(nsplit, a.ntile_bound);
+    constexpr int GRT = pf_group_rt(HP);
+    const dim3 grid(nsplit, a.ntile_bound), block(kPfGroupWaves * 64);
     if (ev0 || ev1)
-      hipExtLaunchKernelGGL((score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, true, false>), grid,
-                            dim3(kPfWaves * 64), 0, st, ev0, ev1, 0, a, 0, 0);
+      hipExtLaunchKernelGGL((score_prefill_kernel<HP, GRT, kPfGroupWaves, kPfKeys, true, false>), grid, block, 0, st,
+                            ev0, ev1, 0, a, 0, 0);
     else
-      hipLaunchKernelGGL((score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, true, false>), grid, dim3(kPfWaves * 64),
-                         0, st, a, 0, 0);
+      hipLaunchKernelGGL((score_prefill_kernel<HP, GRT, kPfGroupWaves, kPfKeys, true, false>), grid, block, 0, st, a,
+                         0, 0);
     return hipGetLastError();
   }
   if (l0) launch(0, score_prefill_kernel<HP, RT, kPfWaves, kPfKeys, false, LISTS>, dim3(ns_full, nq_full), 0, 0);
@@ -458,9 +464,16 @@ static hipError_t launch_hp(const PrefillArgs &a, hipStream_t st, hipEvent_t ev0
   return hipGetLastError();
 }
 
+static int head_slots(int h) { return h <= 1 ? 1 : h <= 2 ? 2 : h <= 4 ? 4 : h <= 8 ? 8 : h <= 16 ? 16 : h <= 32 ? 32 : 64; }
+
 int prefill_queries_per_wg(int h) {
-  const int hp = h <= 1 ? 1 : h <= 2 ? 2 : h <= 4 ? 4 : h <= 8 ? 8 : h <= 16 ? 16 : h <= 32 ? 32 : 64;
+  const int hp = head_slots(h);
   return kPfWaves * pf_rt(hp) * 32 / hp;
+}
+
+int prefill_group_queries_per_wg(int h) {
+  const int hp = head_slots(h);
+  return kPfGroupWaves * pf_group_rt(hp) * 32 / hp;
 }
 
 bool prefill_supported(int h, int ld, int Lmax) {
@@ -539,7 +552,7 @@ __global__ __launch_bounds__(1024) void prefill_tiles_kernel(const int32_t *q_se
 hipError_t launch_prefill_tiles(const int32_t *q_seq, int T, int h, int bound, int2 *tiles, uint32_t *ntiles,
                                 uint32_t *fallback, hipStream_t st) {
   if (T < 1 || bound < 1 || !prefill_supported(h, 1, 1)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prefill_tiles_kernel, dim3(1), dim3(1024), 0, st, q_seq, T, prefill_queries_per_wg(h), bound,
+  hipLaunchKernelGGL(prefill_tiles_kernel, dim3(1), dim3(1024), 0, st, q_seq, T, prefill_group_queries_per_wg(h), bound,
                      tiles, ntiles, fallback);
   return hipGetLastError();
 }

@@ -211,6 +211,11 @@ WORKLOADS = {
         kind="dagger", S=16, L=131072, H=64, B=128, h=8, kc=8192, k=2048),
     "misa_prefill_chunk_4096q_L65536": dict(
         kind="prefill", L=65536, T=4096, H=32, B=128, h=8, k=2048),
+    # several queries per sequence (speculative or batched decode): the rows
+    # of a sequence share one pass over its keys (the multi-query tiling)
+    "misa_multiquery_decode_8x8x32K": dict(
+        kind="decode", S=8, L=32768, H=64, queries_per_seq=8, n_needles=32,
+        B=128, h=8, k=2048),
     # the hierarchical indexer (all heads) and MISA composed with it (the
     # routed heads in both of its stages), on the MISA decode shape; m = 64
     # kept blocks of 128 keys = 8192 candidate tokens per query

@@ -94,10 +94,11 @@ def _load(name):
 
 
 @pytest.mark.parametrize("name", ["tiny_dsa_vs_misa_decode_L4096", "misa_decode_16x128K",
-                                  "misa_prefill_chunk_4096q_L65536"])
+                                  "misa_multiquery_decode_8x8x32K", "misa_prefill_chunk_4096q_L65536"])
 def test_workload_misa(name):
     """The fused MISA call (router, routed scoring, top-k); the prefill chunk
-    takes the tiled router, the 32x32 MFMA scoring and the streamed select."""
+    takes the tiled router, the 32x32 MFMA scoring and the threshold-list
+    select, the multi-query decode batch the MFMA tiling over its tile table."""
     abi = _abi()
     case, cfg, b = _load(name)
     B, h, k = cfg["B"], cfg["h"], cfg["k"]
