@@ -178,7 +178,10 @@ int misa_route(const misa_batch *b, const float *pooled, int32_t B, int32_t h,
  * with heads == NULL, the dense DSA indexer of the Problem Statement).
  *   heads   int32 [T][h] routed head ids, or NULL for all H heads.
  *   scores  fp32 [T][Lmax] (output): I(i) for i <= p_t, -inf for i > p_t.
- * bf16 products, fp32 accumulation.  1 <= h <= H when heads != NULL.
+ * bf16 products, fp32 accumulation.  1 <= h <= H when heads != NULL.  One
+ * sequence with at least 64 rows takes the MFMA tiling of misa_score_topk;
+ * several sequences are scored row by row (this call has no workspace for
+ * the tile table).
  */
 int misa_score(const misa_batch *b, const int32_t *heads, int32_t h,
                float *scores, void *stream);
@@ -203,6 +206,18 @@ int misa_topk(const float *scores, int32_t rows, int32_t ld,
  *   idx     int32 [T][k] (output) selected token ids, val fp32 [T][k]
  *           (output, may be NULL) their scores.
  * 1 <= k <= Lmax.  ws: MISA_OP_SCORE_TOPK.
+ * How it runs (results are the same up to fp32 summation order):
+ *   - one sequence (S = 1), at least 64 rows, at most 64 head slots a query:
+ *     a 32x32 MFMA tiling that reads each key once per tile of queries; with
+ *     5..16 routed heads and at least 256 rows longer than 16384 keys the
+ *     top-k comes from threshold lists the tiling writes instead of score
+ *     rows, and rows those lists cannot settle are rescored one by one;
+ *   - several sequences with at least two rows per sequence on average: the
+ *     same tiling over a table of runs of equal q_seq built on the device,
+ *     so a sequence's rows share one pass over its keys.  Keep the rows of
+ *     a sequence contiguous; otherwise every row is scored on its own
+ *     (still correct);
+ *   - otherwise each row streams its prefix.
  */
 int misa_score_topk(const misa_batch *b, const int32_t *heads, int32_t h,
                     int32_t k, int32_t *idx, float *val, void *ws,
