@@ -596,6 +596,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_flagged_kernel(TopkArgs a) {
 //     ties -- takes the row select);
 //  4. the exactness check (K's digit against every cutoff), then one pass
 //     writes every key >= K, positions from a block scan.
+// above this many outputs a row's merge writes them in runs per wave (fewer
+// cache lines a store); below, the block scan's layout costs less
+constexpr uint32_t kRunOutMin = 4096;
+
 template <bool MAP>
 __global__ __launch_bounds__(kSelThreads) void topk_merge_kernel(TopkArgs a) {
   constexpr int NT = kSelThreads, NW = NT / kWave;
@@ -730,25 +734,50 @@ __global__ __launch_bounds__(kSelThreads) void topk_merge_kernel(TopkArgs a) {
     rowselect_row<MAP, false>(a, r, L);
     return;
   }
-  // every key >= K: exactly kk of them
+  // every key >= K: exactly kk of them, in any order
   uint32_t selbits = 0;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const uint32_t i = (uint32_t)(tid + NT * u);
     if (kk > 0 && i < total && L.cs[i] >= kth) selbits |= 1u << u;
   }
-  const uint32_t mine = (uint32_t)__popc(selbits);
-  uint32_t tot;
-  uint32_t pos = block_scan<NT>(mine, sh, tot) - mine;
+  if (kk > kRunOutMin) {  // uniform
+    // many: wave w's entries of slot u follow those of its slots < u and the
+    // waves' runs follow one another, so each store writes one short run
+    uint32_t wtot = 0;
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    if ((selbits >> u) & 1u) {
-      const uint64_t ck = L.cs[tid + NT * u];
-      if (pos < kk) {
-        irow[pos] = (int32_t)(~(uint32_t)ck);
-        if (vrow) vrow[pos] = key_to_float((uint32_t)(ck >> 32));
+    for (int u = 0; u < PER; ++u) wtot += (uint32_t)__popcll(__ballot((selbits >> u) & 1u));
+    __syncthreads();  // sh is free again
+    if (lane == 0) sh[wave] = wtot;
+    __syncthreads();
+    uint32_t pos = 0;
+    for (int w = 0; w < NW; ++w) pos += w < wave ? sh[w] : 0u;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const bool s_u = (selbits >> u) & 1u;
+      const uint64_t m = __ballot(s_u);
+      if (s_u) {
+        const uint64_t ck = L.cs[tid + NT * u];
+        const uint32_t p = pos + lanes_below(m);
+        irow[p] = (int32_t)(~(uint32_t)ck);
+        if (vrow) vrow[p] = key_to_float((uint32_t)(ck >> 32));
       }
-      ++pos;
+      pos += (uint32_t)__popcll(m);
+    }
+  } else {  // few: each thread's entries side by side, positions from a block scan
+    const uint32_t mine = (uint32_t)__popc(selbits);
+    uint32_t tot;
+    uint32_t pos = block_scan<NT>(mine, sh, tot) - mine;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      if ((selbits >> u) & 1u) {
+        const uint64_t ck = L.cs[tid + NT * u];
+        if (pos < kk) {
+          irow[pos] = (int32_t)(~(uint32_t)ck);
+          if (vrow) vrow[pos] = key_to_float((uint32_t)(ck >> 32));
+        }
+        ++pos;
+      }
     }
   }
   for (int i = (int)kk + tid; i < a.k; i += NT) {

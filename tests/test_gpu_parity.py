@@ -321,8 +321,9 @@ def test_score_topk(S, Lmax, T, H, seed, k):
     assert np.array_equal(np.sort(di, 1), np.sort(np_(dref), 1))
 
 
+@pytest.mark.parametrize("k", [2048, 6000])
 @pytest.mark.parametrize("concentrated", [False, True])
-def test_two_stage_select_on_scored_rows(concentrated):
+def test_two_stage_select_on_scored_rows(concentrated, k):
     """Few long rows take the two-stage select: each scoring workgroup keeps
     its chunk's share of the row's top-k, and the merge takes the top-k of
     the union.  With the top-k spread over the row the union proves the
@@ -332,7 +333,7 @@ def test_two_stage_select_on_scored_rows(concentrated):
     the whole score row.  Both are checked exactly against the kernel's own
     scores and against the oracle's selection."""
     abi = _abi()
-    S, Lmax, T, H, k = 3, 40000, 5, 16, 2048
+    S, Lmax, T, H = 3, 40000, 5, 16
     q_seq = np.array([0, 1, 2, 0, 1], np.int32)
     q_pos = np.array([Lmax - 1, 39000, 17000, 25000, Lmax - 1], np.int32)
     case = synth.random_case(S, Lmax, T, H, seed=41, q_pos=q_pos, q_seq=q_seq)
