@@ -173,9 +173,6 @@ __device__ __forceinline__ void score_row_chunk(const ScoreArgs &a, const int t)
   const int wstart = c0 + wave * 16 * U;
   const int nsteps = wstart < c1 ? (c1 - wstart + stride - 1) / stride : 0;
   uint4 ka[U][4], kb2[U][4];
-  // with the router's last step in the prologue, the first step's keys are
-  // requested before the heads are known (their loads overlap the reduction)
-
 
   auto process_step = [&](int base, const uint4 (&kv)[U][4]) {
     float part[U];
