@@ -69,11 +69,17 @@ template <int E> using epi_t = std::integral_constant<int, E>;
 // the grid into the workgroup space.
 // LISTS: instead of the score rows, every score >= tau[row] goes to the
 // row's threshold list for this key split (kernels.hpp, PrefillArgs::tau) as
-// (score bits, column): the 32 lanes holding a row's columns place their hits
-// side by side (positions from a ballot) after those of the earlier column
-// blocks, so a row's list is one contiguous run and a store touches one or
-// two cache lines; its length (which may pass the capacity: the list
-// overflowed) is written at the end.
+// (score bits, column).  Column blocks are taken in pairs: one lane swap
+// (v_permlane32_swap) trades the upper lane group of the first block's
+// scores for the lower group of the second's, after which a register holds
+// one row over 64 consecutive columns, so the hits' places come from one
+// ballot and the row's hit count is a scalar.  A row's hits lie side by
+// side after those of the earlier blocks, so its list is one contiguous run
+// and a store touches one or two cache lines.  The list stores are issued
+// by every lane (a lane without a hit, or past the capacity, stores out of
+// the buffer's range and is dropped), so the vmcnt waits count them.  The
+// row's hit count (which may pass the capacity: the list overflowed) is
+// written at the end.
 template <int HP, int RT, int NW, int KT, bool GEN, bool LISTS>
 __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, int qtile0, int split0) {
   constexpr bool WIDE = HP > 16;                // a query's slots span both lane groups
@@ -88,10 +94,10 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
   constexpr int TB = KT * 256;                  // bytes per key tile
   constexpr int OUT = RT * 16 / LS;             // scores per lane per column block (one store each)
   static_assert(!WIDE || (RT == 2 && (HP == 32 || HP == 64) && !LISTS), "wide head sets");
-  // stores per lane per column block that the waits count: the score rows'
-  // stores.  List stores are issued only where a lane has a hit and are not
-  // counted: with lists every wait is for all outstanding operations.
-  constexpr int VMO = LISTS ? 0 : OUT;
+  // stores per lane per column block that the waits count: a score row
+  // store per output, or with lists 2 OUT list stores for every second block
+  // (the waits come after an even number of blocks since the last DMA)
+  constexpr int VMO = OUT;
   static_assert(NDMA * 4 * NW == KT && NW % 4 == 0 && NB == 4, "tile shape");
   // the two key-tile buffers are separate arrays so that the compiler can
   // tell reads of one from DMA writes into the other
@@ -145,8 +151,10 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
   uint32_t rowo[OUT];
   int lim[OUT];       // position - l32: key kb + l32 is in the prefix iff kb <= lim
   bool rowok[OUT];
-  float tau[OUT];     // threshold-list cut of the lane's rows (LISTS)
-  uint32_t lcnt[OUT]; // hits of the lane's row so far (the same in the 32 lanes of the row)
+  // LISTS: per row of the wave (2 OUT of them, index 2 o + lane group),
+  // its cut and its hits so far -- both uniform over the wave
+  float rtau[LISTS ? 2 * OUT : 1];
+  uint32_t rcnt[LISTS ? 2 * OUT : 1];
   // (query, head slot) of A row (gg, rr) of tile rt -- also of accumulator r
   // of lane group gg -- and the query of output o.  HP <= 16: tile rt holds
   // queries tile_q0 + gg*QPL + rr/HP, slot rr%HP; HP = 32: tile rt is query
@@ -164,6 +172,8 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
     if constexpr (!WIDE) return qt0 + (wave * RT + o / QPL) * QPT + g * QPL + o % QPL;
     else return qt0 + wave * QPW + o;
   };
+  // the query of output o in lane group gg (LISTS: the row of list register 2 o + gg)
+  auto out_qg = [&](int o, int gg) { return qt0 + (wave * RT + o / QPL) * QPT + gg * QPL + o % QPL; };
   // head id of slot sl of query t: the routed list, or head sl itself (dense)
   auto head_of = [&](int t, int sl) { return a.heads ? a.heads[(size_t)t * a.h + sl] : sl; };
   // Every index is clamped so that all loads of a round are issued together
@@ -205,9 +215,12 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
     rowo[o] = (uint32_t)(((t - qt0) * a.ld + l32) * 4);
     rowok[o] = row_in(t);
     lim[o] = rowok[o] ? pos[o] - l32 : INT_MIN;
-    if constexpr (LISTS) {
-      tau[o] = a.tau[min(t, Tm)];
-      lcnt[o] = 0;
+  }
+  if constexpr (LISTS) {
+#pragma unroll
+    for (int i = 0; i < 2 * OUT; ++i) {
+      rtau[i] = a.tau[min(out_qg(i / 2, i % 2), Tm)];
+      rcnt[i] = 0;
     }
   }
   // wide head sets: the lane group that stores output o (the other holds
@@ -249,29 +262,50 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
   const __amdgpu_buffer_rsrc_t srs =
       __builtin_amdgcn_make_buffer_rsrc((void *)wg_rows, (short)0, (int)((uint32_t)QWG * a.ld * 4u), 0x00020000);
   // the workgroup's threshold lists for this split: rows qt0.. of
-  // [split][T][tcap] entries
+  // [split][T][tcap] entries, one buffer over the workgroup's valid rows; a
+  // row's list starts at its scalar offset (which the range check counts).
+  // A lane without a hit stores at an offset past the range (dropped), and
+  // once a row's hits pass the capacity no lane stores: the merge leaves an
+  // overflowed list unread (the row is rescored), so its contents are free.
   const int split_id = blockIdx.x + split0;
   uint2 *const wg_lists = LISTS ? a.tlists + ((size_t)split_id * a.T + qt0) * a.tcap : nullptr;
-  const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)wg_lists, (short)0, LISTS ? (int)((uint32_t)min(QWG, a.T - qt0) * (uint32_t)a.tcap * 8u) : 0,
-      0x00020000);
-  // the first byte of the list of the lane's output o (row out_q(o) - qt0)
   const uint32_t lrow = LISTS ? (uint32_t)a.tcap * 8u : 0u;
-  auto lbase = [&](int o) { return (uint32_t)(out_q(o) - qt0) * lrow; };
+  const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)wg_lists, (short)0, LISTS ? (int)((uint32_t)min(QWG, a.T - qt0) * lrow) : 0, 0x00020000);
+  // list register i of a block pair (row out_qg(i / 2, i % 2), columns
+  // x0 .. x0 + 63): its hits after the row's earlier ones
+  auto list_put = [&](int i, float v, int x0) __attribute__((always_inline)) {
+    const bool hit = v >= rtau[i];  // (false for the NaN of a masked column)
+    const uint64_t m = __ballot(hit);
+    const uint32_t nh = (uint32_t)__popcll(m);
+    const bool room = rcnt[i] + nh <= (uint32_t)a.tcap;  // uniform
+    const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    const uint32_t voff = hit && room ? (rcnt[i] + below) * 8u : 0x80000000u;
+    rcnt[i] += nh;
+    const u32x2 ent = {__float_as_uint(v), (uint32_t)(x0 + lane)};
+    __builtin_amdgcn_raw_buffer_store_b64(ent, lrs, voff, (int)((uint32_t)(out_qg(i / 2, i % 2) - qt0) * lrow), 0);
+  };
   const f32x16 zero = {};
   f32x16 acc[2][RT];
   uint4 bfr[8];
-  float sc[OUT];
+  // the head sums of a block; with lists, [0] and [1] hold the two blocks of a pair
+  float scs[LISTS ? 2 : 1][OUT];
 
   // one 32-key column block: the MFMA chain of `cur` from bfr, each fragment
   // replaced right after its MFMAs by the same fragment of the next block
   // (NEXT_CB: that block's index in the buffer raddr points at), and the
   // previous block's epilogue (head sums of `prev`, then stores at key base
-  // kbp) spread over the eight steps so the vector ALU runs beside the MFMAs
-  auto block = [&](f32x16 (&cur)[RT], const f32x16 (&prev)[RT], auto next_buf, auto next_cb, int kbp, auto epi) {
+  // kbp) spread over the eight steps so the vector ALU runs beside the MFMAs.
+  // PAIR (lists): 0 for the first block of a pair, 1 for the second, whose
+  // epilogue also places the pair's hits.
+  // (forced inline: an outlined call would pass the accumulators through scratch)
+  auto block = [&](f32x16 (&cur)[RT], const f32x16 (&prev)[RT], auto next_buf, auto next_cb, int kbp, auto epi,
+                   auto pair) __attribute__((always_inline)) {
     constexpr int NEXT = decltype(next_cb)::value;
     const char *const nb = buf_of(next_buf);
     constexpr int EPI = decltype(epi)::value;
+    constexpr int PAIR = LISTS ? decltype(pair)::value : 0;
+    float(&sc)[OUT] = scs[PAIR];
 
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -305,22 +339,15 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
                 *(float *)(wg_rows + (size_t)kbp * 4 + rowo[o]) = in ? sc[o] : -INFINITY;
             }
             if constexpr (LISTS) {
-              const bool hit = in && sc[o] >= tau[o];
-              // the hit's place among its row's hits of this block: lanes
-              // 0..31 hold row g = 0, lanes 32..63 row g = 1
-              const uint64_t hm = __ballot(hit);
-              const uint32_t hlo = (uint32_t)hm, hhi = (uint32_t)(hm >> 32);
-              const uint32_t below =
-                  __builtin_amdgcn_mbcnt_hi(hhi, __builtin_amdgcn_mbcnt_lo(hlo, 0u)) - (g ? (uint32_t)__popc(hlo) : 0u);
-              const uint32_t slot = lcnt[o] + below;
-              lcnt[o] += g ? (uint32_t)__popc(hhi) : (uint32_t)__popc(hlo);
-              if (hit && slot < (uint32_t)a.tcap) {
-                const u32x2 ent = {__float_as_uint(sc[o]), (uint32_t)(kbp + l32)};
-                const uint32_t off = lbase(o) + slot * 8u;
-                if (EPI == kEpiGeneric)
-                  *(u32x2 *)((char *)wg_lists + off) = ent;
-                else
-                  __builtin_amdgcn_raw_buffer_store_b64(ent, lrs, off, 0, 0);
+              if (EPI != kEpiFull && !in) sc[o] = __uint_as_float(0x7FC00000u);  // NaN: never a hit
+              if constexpr (PAIR == 1) {
+                // lanes 32..63 of the first block's sums trade places with
+                // lanes 0..31 of the second's: [0] is then row out_qg(o, 0),
+                // [1] row out_qg(o, 1), each over the pair's 64 columns
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(scs[0][o]),
+                                                                 __float_as_uint(scs[1][o]), false, false);
+                list_put(2 * o, __uint_as_float(sw[0]), kbp - 32);
+                list_put(2 * o + 1, __uint_as_float(sw[1]), kbp - 32);
               }
             }
           }
@@ -335,14 +362,16 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
   // and every wave holds its fragments of tile it, so after the barrier the
   // DMA of tile it+2 may overwrite buffer it % 2 and the last block reads
   // tile it+1's first fragments.
-  auto tile = [&](int it, auto prev_epi, auto cur_epi, auto buf) {
+  auto tile = [&](int it, auto prev_epi, auto cur_epi, auto buf) __attribute__((always_inline)) {
     constexpr int PE = decltype(prev_epi)::value, CE = decltype(cur_epi)::value, B = decltype(buf)::value;
     using cur_b = std::integral_constant<int, B>;
     using nxt_b = std::integral_constant<int, B ^ 1>;
     const int kt = k0 + it * KT;
-    block(acc[0], acc[1], cur_b{}, std::integral_constant<int, 1>{}, kt - 32, prev_epi);
-    block(acc[1], acc[0], cur_b{}, std::integral_constant<int, 2>{}, kt, cur_epi);
-    block(acc[0], acc[1], cur_b{}, std::integral_constant<int, 3>{}, kt + 32, cur_epi);
+    using first = std::integral_constant<int, 0>;
+    using second = std::integral_constant<int, 1>;
+    block(acc[0], acc[1], cur_b{}, std::integral_constant<int, 1>{}, kt - 32, prev_epi, second{});
+    block(acc[1], acc[0], cur_b{}, std::integral_constant<int, 2>{}, kt, cur_epi, first{});
+    block(acc[0], acc[1], cur_b{}, std::integral_constant<int, 3>{}, kt + 32, cur_epi, second{});
     if (PE == kEpiGeneric || CE == kEpiGeneric) {
       PF_WAIT_VM(0);
     } else if (PE == kEpiNone) {
@@ -352,7 +381,7 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
     }
     __syncthreads();
     if (it + 2 < ntile) dma_tile(it + 2, cur_b{});
-    block(acc[1], acc[0], nxt_b{}, std::integral_constant<int, 0>{}, kt + 64, cur_epi);
+    block(acc[1], acc[0], nxt_b{}, std::integral_constant<int, 0>{}, kt + 64, cur_epi, first{});
   };
   if (ntile > 0) {
     dma_tile(0, std::integral_constant<int, 0>{});
@@ -390,13 +419,13 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
     // the last block's epilogue (its MFMAs ran in the final tile's last block)
     const int kbp = k0 + ntile * KT - 32;
     f32x16 dummy[RT];
-    block(dummy, acc[1], b0{}, std::integral_constant<int, 0>{}, kbp, epi_t<E>{});
+    block(dummy, acc[1], b0{}, std::integral_constant<int, 0>{}, kbp, epi_t<E>{}, std::integral_constant<int, 1>{});
   }
   if constexpr (LISTS) {  // the rows' hit counts: [split][T]
 #pragma unroll
-    for (int o = 0; o < OUT; ++o) {
-      const int t = out_q(o);
-      if (l32 == 0 && t < a.T) a.tcount[(size_t)split_id * a.T + t] = lcnt[o];
+    for (int i = 0; i < 2 * OUT; ++i) {
+      const int t = out_qg(i / 2, i % 2);
+      if (lane == 0 && t < a.T) a.tcount[(size_t)split_id * a.T + t] = rcnt[i];
     }
   }
   if (LISTS) return;  // no score rows

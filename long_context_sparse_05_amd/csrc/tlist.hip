@@ -229,7 +229,14 @@ __global__ __launch_bounds__(kTmThreads) void tlist_merge_kernel(TlistArgs a) {
     wb = ds;
     if (inb <= (uint32_t)NT || ds == 0) break;
   }
-  if (tid == 0) *flag = 0u;
+  if (inb > (uint32_t)NT) {  // uniform: equal composite keys, which valid lists never hold
+    flag_row();
+    return;
+  }
+  if (tid == 0) {
+    *flag = 0u;
+    red[0] = red[1] = 0xFFFFFFFFu;  // no composite key is all ones (NaN never reaches tau)
+  }
   // the crossing digit's keys into the histogram's words, ranked among themselves
   uint64_t *bkeys = (uint64_t *)lh;
 #pragma unroll
@@ -253,6 +260,10 @@ __global__ __launch_bounds__(kTmThreads) void tlist_merge_kernel(TlistArgs a) {
   }
   __syncthreads();
   const uint64_t kth = ((const uint64_t *)red)[0];
+  if (kth == ~0ull) {  // uniform: no key of rank kk, which valid lists always have
+    flag_row();
+    return;
+  }
   // every key >= K: exactly kk of them.  Output order is free: wave w's
   // selected entries of slot u follow those of its slots < u, the waves'
   // runs one after another, so each store instruction writes one short run.
@@ -270,8 +281,8 @@ __global__ __launch_bounds__(kTmThreads) void tlist_merge_kernel(TlistArgs a) {
   for (int u = 0; u < PER; ++u) {
     const bool s_u = ((valid >> u) & 1u) && ck[u] >= kth;
     const uint64_t m = __ballot(s_u);
-    if (s_u) {
-      const uint32_t pos = base + lanes_below(m);
+    const uint32_t pos = base + lanes_below(m);
+    if (s_u && pos < kk) {  // (exactly kk are selected; the bound keeps a bad list in the row)
       irow[pos] = (int32_t)(~(uint32_t)ck[u]);
       if (vrow) vrow[pos] = key_to_float((uint32_t)(ck[u] >> 32));
     }
