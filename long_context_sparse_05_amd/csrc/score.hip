@@ -48,7 +48,7 @@ template <int HT, bool GATHER, bool ROUTE, int U, int NW>
 __device__ __forceinline__ void score_row_chunk(const ScoreArgs &a, const int t) {
   constexpr int NT = NW * 64;
   static_assert(!(ROUTE && GATHER), "the router prologue serves direct rows");
-  __shared__ uint32_t lds_hist[kHistBins];
+  __shared__ alignas(16) uint32_t lds_hist[kHistBins];
   __shared__ float rred[ROUTE ? 4 : 1][MISA_MAX_HEADS_DEV];  // router prologue scratch
   __shared__ float rgs[ROUTE ? MISA_MAX_HEADS_DEV : 1];
   __shared__ int32_t rheads[ROUTE ? MISA_MAX_HEADS_DEV : 1];  // the routed heads

@@ -47,45 +47,58 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t *sh, uint32_
   return base + incl;
 }
 
-// Threshold digit from a 4096-bin histogram in LDS.  The first 256 threads
-// own 16 consecutive bins each, counted from the top; the others add zero.
-// sh needs NT/64 + 4 words.
+// Threshold digit from a 4096-bin histogram in LDS, counted from the top:
+// the bin holding the k-th largest key.  The first wave alone resolves it
+// (lane l sums the 64 bins [4096 - 64 (l + 1), 4096 - 64 l); a scan over
+// the lanes finds the lane whose bins cross k, and a scan over that lane's
+// 64 bins, one per lane, finds the bin); the workgroup reads the result
+// from sh[NT/64 .. NT/64 + 2] between two barriers, so the caller may reuse
+// those words at once.  sh needs NT/64 + 3 words; call with uniform control
+// flow.
 template <int NT>
 __device__ __forceinline__ Thresh threshold_from_lds(const uint32_t *lh, uint32_t k, uint32_t *sh) {
-  static_assert(NT >= 256, "one thread per 16 bins");
-  const int tid = threadIdx.x;
-  const int top = kHistBins - 1 - 16 * tid;
-  uint32_t v[16];
-  uint32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    v[i] = tid < 256 ? lh[top - i] : 0u;
-    s += v[i];
-  }
-  uint32_t total;
-  const uint32_t incl = block_scan<NT>(s, sh, total);
-  const uint32_t excl = incl - s;
-  const uint32_t kk = min(k, total);
+  static_assert(NT % kWave == 0 && kHistBins == 64 * kWave, "one wave, 64 bins a lane");
   uint32_t *res = sh + NT / kWave;
-  if (kk > 0 && excl < kk && kk <= incl) {
-    uint32_t cum = excl;
+  if (threadIdx.x < kWave) {
+    const int lane = (int)threadIdx.x;
+    const int lo = kHistBins - 64 * (lane + 1);
+    uint32_t s = 0;
+    // (neighbouring lanes start at different 4-bin chunks: lanes 256 bytes
+    // apart would all hit one bank group)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (cum + v[i] >= kk) {
-        res[0] = (uint32_t)(top - i);
-        res[1] = cum;
-        res[2] = v[i];
-        break;
-      }
-      cum += v[i];
+    for (int j = 0; j < 16; ++j) {
+      const uint4 v = *(const uint4 *)(lh + lo + 4 * ((j + lane) & 15));
+      s += (v.x + v.y) + (v.z + v.w);
+    }
+    const uint32_t incl = wave_incl_scan(s);
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+    const uint32_t kk = min(k, total);
+    uint32_t b1 = kHistBins, above = 0, eq = 0;
+    if (kk > 0) {
+      const int L = __ffsll((unsigned long long)__ballot(incl >= kk)) - 1;
+      const uint32_t aboveL = (uint32_t)__builtin_amdgcn_readlane((int)(incl - s), L);
+      const int loL = kHistBins - 64 * (L + 1);
+      const uint32_t x = lh[loL + 63 - lane];  // lane i: bin loL + 63 - i
+      const uint32_t inc2 = wave_incl_scan(x) + aboveL;
+      const int i = __ffsll((unsigned long long)__ballot(inc2 >= kk)) - 1;
+      b1 = (uint32_t)(loL + 63 - i);
+      above = (uint32_t)__builtin_amdgcn_readlane((int)(inc2 - x), i);
+      eq = (uint32_t)__builtin_amdgcn_readlane((int)x, i);
+    }
+    if (lane == 0) {
+      res[0] = b1;
+      res[1] = above;
+      res[2] = eq;
     }
   }
   __syncthreads();
   Thresh th;
-  th.kk = kk;
-  th.b1 = kk ? (int)res[0] : kHistBins;
-  th.above = kk ? res[1] : 0;
-  th.eq = kk ? res[2] : 0;
+  th.b1 = (int)res[0];
+  th.above = res[1];
+  th.eq = res[2];
+  // the bins below the crossing one are empty when the histogram holds
+  // fewer than k keys, so min(k, above + eq) is min(k, total)
+  th.kk = th.b1 < kHistBins ? min(k, th.above + th.eq) : 0u;
   __syncthreads();
   return th;
 }

@@ -113,7 +113,7 @@ constexpr int kTmPer = kTlistUnionCap / kTmThreads;
 __global__ __launch_bounds__(kTmThreads) void tlist_merge_kernel(TlistArgs a) {
   constexpr int NT = kTmThreads, NW = NT / kWave, PER = kTmPer, NB = kHistBins;
   static_assert(kMaxTlists <= kWave && PER <= NT, "one wave scans the lists");
-  __shared__ uint32_t lh[NB];  // histogram, then the crossing bin's keys (64-bit)
+  __shared__ alignas(16) uint32_t lh[NB];  // histogram, then the crossing bin's keys (64-bit)
   __shared__ uint32_t sh[NW + 8];
   __shared__ uint32_t slen[kMaxTlists], sfirst[kMaxTlists];
   __shared__ alignas(8) uint32_t red[4];  // [0] overflow [1] largest key [2] crossing-bin keys; then K

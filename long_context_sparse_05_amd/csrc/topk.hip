@@ -40,7 +40,7 @@ constexpr int kSelCompact = 2048;   // survivors compacted after each pass
 // The LDS of a 1024-thread row select, declared once by each kernel that
 // runs one (the merge kernel reuses it, so its fallback to the exact row
 // select needs no second copy).
-struct SelLds {
+struct alignas(16) SelLds {
   uint64_t cs[kSelCap];
   uint64_t cs2[kSelCompact];
   uint32_t hs[256];
@@ -792,7 +792,7 @@ template <bool MAP>
 __global__ __launch_bounds__(256) void topk_lists_kernel(TopkArgs a) {
   constexpr int NT = 256, PER = kListChunk / NT;
   __shared__ float sc[kListChunk];
-  __shared__ uint32_t lh[kHistBins];
+  __shared__ alignas(16) uint32_t lh[kHistBins];
   __shared__ int32_t tk[MAP ? kListChunk : 1];
   __shared__ uint32_t sh[2 * NT / kWave + 9];
   const int r = blockIdx.y, tid = threadIdx.x;
