@@ -266,7 +266,9 @@ __global__ __launch_bounds__(kTmThreads) void tlist_merge_kernel(TlistArgs a) {
   }
   // every key >= K: exactly kk of them.  Output order is free: wave w's
   // selected entries of slot u follow those of its slots < u, the waves'
-  // runs one after another, so each store instruction writes one short run.
+  // runs one after another -- staged in the (now free) histogram words when
+  // they fit, then written with coalesced stores, else written directly.
+  const bool stage = kk <= (uint32_t)(NB / 2);  // uniform
   uint32_t wtot = 0;
 #pragma unroll
   for (int u = 0; u < PER; ++u)
@@ -283,10 +285,22 @@ __global__ __launch_bounds__(kTmThreads) void tlist_merge_kernel(TlistArgs a) {
     const uint64_t m = __ballot(s_u);
     const uint32_t pos = base + lanes_below(m);
     if (s_u && pos < kk) {  // (exactly kk are selected; the bound keeps a bad list in the row)
-      irow[pos] = (int32_t)(~(uint32_t)ck[u]);
-      if (vrow) vrow[pos] = key_to_float((uint32_t)(ck[u] >> 32));
+      if (stage) {
+        bkeys[pos] = ck[u];
+      } else {
+        irow[pos] = (int32_t)(~(uint32_t)ck[u]);
+        if (vrow) vrow[pos] = key_to_float((uint32_t)(ck[u] >> 32));
+      }
     }
     base += (uint32_t)__popcll(m);
+  }
+  if (stage) {
+    __syncthreads();
+    for (uint32_t i = (uint32_t)tid; i < kk; i += NT) {
+      const uint64_t c = bkeys[i];
+      irow[i] = (int32_t)(~(uint32_t)c);
+      if (vrow) vrow[i] = key_to_float((uint32_t)(c >> 32));
+    }
   }
   for (int i = (int)kk + tid; i < a.k; i += NT) {
     irow[i] = -1;
