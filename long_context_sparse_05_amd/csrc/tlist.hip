@@ -64,8 +64,10 @@ __global__ __launch_bounds__(256) void tlist_gather_kernel(const uint16_t *keys,
 
 // One wave per row, four rows per workgroup: tau[t] = the r-th largest of
 // the row's NS sample scores, its order key rounded down to a multiple of
-// 256 (a lower bound): the largest such key K with at least r sample keys
-// >= K, found bit by bit from the top, each step one count over the row.
+// 65536 (a lower bound, at most about 1% below that score: the float keeps
+// its sign, exponent and 7 mantissa bits): the largest such key K with at
+// least r sample keys >= K, found bit by bit from the top, each step one
+// count over the row.
 // r >= NS (a short row) gives -inf: every score is kept.
 template <int NS>
 __global__ __launch_bounds__(256) void tlist_tau_kernel(const float *ss, const int32_t *q_pos, int T, int k,
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(256) void tlist_tau_kernel(const float *ss, const i
 #pragma unroll
   for (int u = 0; u < PER; ++u) key[u] = order_key(row[lane + kWave * u]);
   uint32_t K = 0;
-  for (int bit = 31; bit >= 8; --bit) {
+  for (int bit = 31; bit >= 16; --bit) {
     const uint32_t cand = K | (1u << bit);
     uint32_t c = 0;
 #pragma unroll
@@ -179,8 +181,10 @@ __global__ __launch_bounds__(kTmThreads) void tlist_merge_kernel(TlistArgs a) {
       const uint32_t j = (starts ? (uint32_t)u - first : 0u) * NT + tid;
       const bool v = u < (int)slots && j < len;
       if (v) valid |= 1u << u;
-      // (a slot without an entry reads the list's first: one cache line for all)
-      e[u] = a.tlists[((size_t)l * a.T + r) * a.tcap + (v ? j : 0u)];
+      // (a slot of a list past its entries reads the list's first; slots past
+      // the row's last list load nothing: `slots` is uniform)
+      e[u] = make_uint2(0u, 0u);
+      if (u < (int)slots) e[u] = a.tlists[((size_t)l * a.T + r) * a.tcap + (v ? j : 0u)];
     }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
