@@ -94,6 +94,7 @@ TLIST_CASES = [
     (30001, 1000, 16, 5, 300, "random", "plain"),     # ragged keys and queries, h < the tile's slots
     (20000, 2048, 8, 6, 128, "tail", "plain"),
     (24576, 1024, 32, 16, 1024, "tail", "plain"),
+    (49152, 2048, 16, 8, 2500, "tail", "plain"),     # k past the merge's LDS staging: written directly
     (32768, 1024, 16, 8, 512, "tail", "sample_high"),
     (24000, 1024, 16, 8, 256, "tail", "sample_zero"),
 ]
