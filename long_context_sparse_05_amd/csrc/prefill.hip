@@ -98,7 +98,7 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
   // store per output, or with lists 2 OUT list stores for every second block
   // (the waits come after an even number of blocks since the last DMA)
   constexpr int VMO = OUT;
-  static_assert(NDMA * 4 * NW == KT && NW % 4 == 0 && NB == 4, "tile shape");
+  static_assert(NDMA * 4 * NW == KT && NW % 4 == 0 && NB % 2 == 0 && NB >= 4, "tile shape");
   // the two key-tile buffers are separate arrays so that the compiler can
   // tell reads of one from DMA writes into the other
   __shared__ uint4 ktile0[TB / 16], ktile1[TB / 16];
@@ -369,19 +369,30 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(PrefillArgs a, i
     const int kt = k0 + it * KT;
     using first = std::integral_constant<int, 0>;
     using second = std::integral_constant<int, 1>;
+    // block j (0 .. NB-2) of the tile runs its MFMAs on acc[j % 2] and the
+    // epilogue of block j - 1 (block 0: the previous tile's last); even
+    // blocks close a pair of epilogues
     block(acc[0], acc[1], cur_b{}, std::integral_constant<int, 1>{}, kt - 32, prev_epi, second{});
-    block(acc[1], acc[0], cur_b{}, std::integral_constant<int, 2>{}, kt, cur_epi, first{});
-    block(acc[0], acc[1], cur_b{}, std::integral_constant<int, 3>{}, kt + 32, cur_epi, second{});
+    auto mid = [&](auto self, auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (j <= NB - 2) {
+        block(acc[j & 1], acc[(j + 1) & 1], cur_b{}, std::integral_constant<int, j + 1>{}, kt + 32 * (j - 1), cur_epi,
+              std::integral_constant<int, (j & 1) ? 0 : 1>{});
+        self(self, std::integral_constant<int, j + 1>{});
+      }
+    };
+    mid(mid, std::integral_constant<int, 1>{});
     if (PE == kEpiGeneric || CE == kEpiGeneric) {
       PF_WAIT_VM(0);
     } else if (PE == kEpiNone) {
-      PF_WAIT_VM((NB - 2) * VMO < 63 ? (NB - 2) * VMO : 63);
+      PF_WAIT_VM((NB - 2) * VMO < 63 ? (NB - 2) * VMO : 63);  // (fewer is only more conservative)
     } else {
       PF_WAIT_VM(NB * VMO < 63 ? NB * VMO : 63);
     }
     __syncthreads();
     if (it + 2 < ntile) dma_tile(it + 2, cur_b{});
-    block(acc[1], acc[0], nxt_b{}, std::integral_constant<int, 0>{}, kt + 64, cur_epi, first{});
+    block(acc[(NB - 1) & 1], acc[NB & 1], nxt_b{}, std::integral_constant<int, 0>{}, kt + 32 * (NB - 2), cur_epi,
+          first{});
   };
   if (ntile > 0) {
     dma_tile(0, std::integral_constant<int, 0>{});
