@@ -37,10 +37,13 @@ namespace misa {
 constexpr int kKeyRowLds = 272;  // bytes per key row in the LDS tile (256 + 16)
 // Waves per workgroup: eight where one 16-row head tile keeps a wave within
 // 128 registers (two workgroups, sixteen waves, per CU: more key loads in
-// flight), four otherwise.
-template <int HT, bool GATHER>
+// flight), and for direct rows of four tiles (64 heads: 200 registers, two
+// waves per SIMD, about 256 workgroups of 4096 keys -- 46.6 -> 46.0 us at
+// 32 x 32768 keys); four otherwise.  (RLIST launches keep four: eight would
+// spill there.)
+template <int HT, bool GATHER, bool RLIST = false>
 constexpr int score_waves() {
-  return HT == 1 && !GATHER ? 8 : 4;
+  return !GATHER && !RLIST && (HT == 1 || HT == 4) ? 8 : 4;
 }
 
 // One (chunk, row) of the scoring: the body of score_rows_kernel.
@@ -285,7 +288,7 @@ static hipError_t launch_ht(const ScoreArgs &a, hipStream_t st, hipEvent_t ev0, 
   if (a.rowcount) {  // (at most 64 heads: rows a prefill or grouped call hands back)
     if constexpr (HT <= 4 && !GATHER && !ROUTE) {
       if (!a.rowcount || ev0 || ev1 || a.chunk > kMaxScoreChunk) return hipErrorInvalidValue;
-      constexpr int U = 2, NW = score_waves<HT, false>();
+      constexpr int U = 2, NW = score_waves<HT, false, true>();
       const dim3 grid((a.ncols + a.chunk - 1) / a.chunk, a.T < kRowListGrid ? a.T : kRowListGrid);
       hipLaunchKernelGGL((score_rows_kernel<HT, false, false, U, NW, true>), grid, dim3(NW * 64), 0, st, a);
       return hipGetLastError();
