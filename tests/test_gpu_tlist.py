@@ -61,6 +61,8 @@ def _case(Lmax, T, H, seed, positions, structure):
     rng = np.random.default_rng(seed + 3)
     if positions == "tail":
         q_pos = np.arange(Lmax - T, Lmax, dtype=np.int32)
+    elif positions == "spread":  # short rows (n < k: every score listed), medium rows (lists overflow), long rows
+        q_pos = np.sort(rng.integers(0, Lmax, size=T)).astype(np.int32)
     else:
         q_pos = np.sort(rng.integers(Lmax // 2, Lmax, size=T)).astype(np.int32)
     case = synth.random_case(1, Lmax, T, H, seed=seed, q_pos=q_pos, q_seq=np.zeros(T, np.int32))
@@ -95,6 +97,7 @@ TLIST_CASES = [
     (20000, 2048, 8, 6, 128, "tail", "plain"),
     (24576, 1024, 32, 16, 1024, "tail", "plain"),
     (49152, 2048, 16, 8, 2500, "tail", "plain"),     # k past the merge's LDS staging: written directly
+    (32768, 1024, 16, 8, 512, "spread", "plain"),     # prefixes from 1 key to the whole sequence
     (32768, 1024, 16, 8, 512, "tail", "sample_high"),
     (24000, 1024, 16, 8, 256, "tail", "sample_zero"),
 ]
@@ -131,7 +134,17 @@ def test_prefill_threshold_list_select(Lmax, T, H, h, k, positions, structure):
             for i, v in zip(idx[t], val[t]):
                 if i >= 0:
                     assert abs(float(v) - sc[t, i]) <= parity.REL * (abs(float(sc[t, i])) + sb)
-    if structure == "plain":
+    if structure == "plain" and positions == "spread":
+        # rows too short for the sample to bound (r >= NS: tau = -inf, among
+        # them every row with at most k keys) go to the rescoring.  The
+        # sample spans only the shortest prefix (a few keys here), so a long
+        # row's tau may miss too and take the rescoring (every row was
+        # checked above); most long rows are still settled by their lists
+        m = k * NS / n_valid.astype(np.float64)
+        short = np.ceil(m + 4.0 * np.sqrt(m) + 8.0) >= NS
+        assert short.any() and np.all(flags[short] == 1)
+        assert flags[n_valid >= Lmax // 2].mean() <= 0.25
+    elif structure == "plain":
         # every row is settled by its lists (ties at the k-th score -- the
         # exact zeros of rows whose weights are all negative -- included)
         assert flags.mean() <= 0.01, flags.mean()
