@@ -401,15 +401,33 @@ size_t grouped_bytes(const misa_batch *b) {
   return b->S > 1 ? align_up((size_t)b->T * sizeof(int2)) + kAlign : 0;
 }
 
-// The grouped scoring into sc [T][Lmax] (gws: grouped_bytes of workspace).
+// The grouped scoring's tile table: rows per tile, the grid's bound on the
+// tiles, and where the table and its counts sit in its workspace.
+struct GroupedTiles {
+  int qwg, bound;
+  int2 *tiles;
+  uint32_t *cnt;
+};
+GroupedTiles grouped_tiles(const misa_batch *b, int nh, void *gws) {
+  GroupedTiles g;
+  g.qwg = prefill_group_queries_per_wg(nh);
+  g.bound = std::min(b->T, (b->T + g.qwg - 1) / g.qwg + b->S);
+  g.tiles = (int2 *)gws;
+  g.cnt = (uint32_t *)((char *)gws + align_up((size_t)b->T * sizeof(int2)));
+  return g;
+}
+
+// The grouped scoring into sc [T][Lmax] (gws: grouped_bytes of workspace);
+// tiles_built: the router's final kernel already built the tile table.
 int grouped_score(const misa_batch *b, const int32_t *heads, int h, float *sc, void *gws, hipStream_t st,
-                  void *ev_start = nullptr, void *ev_stop = nullptr) {
+                  void *ev_start = nullptr, void *ev_stop = nullptr, bool tiles_built = false) {
   const int nh = heads ? h : b->H;
-  const int qwg = prefill_group_queries_per_wg(nh);
-  const int bound = std::min(b->T, (b->T + qwg - 1) / qwg + b->S);
-  int2 *tiles = (int2 *)gws;
-  uint32_t *cnt = (uint32_t *)((char *)gws + align_up((size_t)b->T * sizeof(int2)));
-  if (launch_prefill_tiles(b->q_seq, b->T, nh, bound, tiles, cnt, cnt + 1, st) != hipSuccess) return MISA_ERR_HIP;
+  const GroupedTiles gt = grouped_tiles(b, nh, gws);
+  const int bound = gt.bound;
+  int2 *tiles = gt.tiles;
+  uint32_t *cnt = gt.cnt;
+  if (!tiles_built && launch_prefill_tiles(b->q_seq, b->T, nh, bound, tiles, cnt, cnt + 1, st) != hipSuccess)
+    return MISA_ERR_HIP;
   PrefillArgs p = make_prefill_args(b, heads, h, sc);
   p.q_seq = b->q_seq;
   p.tiles = tiles;
@@ -660,13 +678,21 @@ int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t
   const TlistLayout TL = tlist_layout(b, h, k);
   if (ws_bytes < rbytes + L.total + TL.total + grouped_bytes(b)) return MISA_ERR_WORKSPACE;
   void *sws = (char *)ws + rbytes;
-  const RouteArgs ra = make_route_args(b, pooled, B, h, mode, heads, head_score, ws);
+  RouteArgs ra = make_route_args(b, pooled, B, h, mode, heads, head_score, ws);
   // many queries of one sequence: the tiled router writes the heads; the
-  // prefill and grouped tilings read them from memory; otherwise the router
-  // kernel leaves partial sums that the scoring kernel's prologue reduces
-  // and ranks
+  // prefill and grouped tilings read them from memory (the grouped one's
+  // tile table built by one more workgroup of the router's final kernel);
+  // otherwise the router kernel leaves partial sums that the scoring
+  // kernel's prologue reduces and ranks
   const bool tiled_router = route_tiled(b), prefill = use_prefill(b, heads, h);
   const bool grouped = !prefill && use_grouped(b, heads, h);
+  if (grouped && !tiled_router) {
+    const GroupedTiles gt = grouped_tiles(b, h, (char *)sws + L.total + TL.total);
+    ra.tiles = gt.tiles;
+    ra.tcount = gt.cnt;
+    ra.tqwg = gt.qwg;
+    ra.tbound = gt.bound;
+  }
   const bool in_prologue = !tiled_router && !prefill && !grouped;
   hipError_t re = tiled_router          ? launch_route_tile(ra, (hipStream_t)stream)
                   : (prefill || grouped) ? launch_route(ra, (hipStream_t)stream)
@@ -676,7 +702,8 @@ int misa_indexer_ev(const misa_batch *b, const float *pooled, int32_t B, int32_t
     return prefill_select(b, heads, h, k, idx, val, sws, L, TL, (hipStream_t)stream, ev_start, ev_stop);
   if (grouped) {
     float *sc = (float *)((char *)sws + L.scores);
-    rc = grouped_score(b, heads, h, sc, (char *)sws + L.total + TL.total, (hipStream_t)stream, ev_start, ev_stop);
+    rc = grouped_score(b, heads, h, sc, (char *)sws + L.total + TL.total, (hipStream_t)stream, ev_start, ev_stop,
+                       ra.tiles != nullptr);
     if (rc) return rc;
     return run_select(nullptr, sc, b->T, b->Lmax, b->q_pos, 1, nullptr, k, idx, val, sws, L, (hipStream_t)stream);
   }

@@ -173,6 +173,12 @@ struct RouteArgs {
   float *partial;          // [T][nchunks + 1][H]
   int32_t *heads;          // [T][h]
   float *g;                // [T][H] or nullptr
+  // optional, launch_route: the tile table of the grouped scoring built by
+  // one more workgroup of the final kernel (tiles.hpp); tcount[0] = tiles,
+  // tcount[1] = the fallback row count
+  int2 *tiles;
+  uint32_t *tcount;
+  int tqwg, tbound;
   int S, Lmax, T, H, B, h, mode, Mmax, nchunks;
 };
 constexpr int kRouteChunk = 64;  // complete blocks per router workgroup

@@ -45,6 +45,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "select.hpp"
+#include "tiles.hpp"
 
 namespace misa {
 
@@ -559,34 +560,7 @@ __global__ __launch_bounds__(1024) void prefill_tiles_kernel(const int32_t *q_se
   constexpr int NT = 1024;
   __shared__ int smax[NT];
   __shared__ uint32_t sh[NT / kWave + 4];
-  const int tid = threadIdx.x;
-  int carry_rs = 0;
-  uint32_t carry_n = 0;
-  for (int base = 0; base < T; base += NT) {
-    const int t = base + tid;
-    const int q = t < T ? q_seq[t] : 0;
-    smax[tid] = (t < T && (t == 0 || q != q_seq[t - 1])) ? t : -1;
-    __syncthreads();
-    for (int off = 1; off < NT; off <<= 1) {
-      const int v = tid >= off ? smax[tid - off] : -1;
-      __syncthreads();
-      smax[tid] = max(smax[tid], v);
-      __syncthreads();
-    }
-    const int rs = max(smax[tid], carry_rs);  // the row's run start
-    const uint32_t ts = (t < T && (t - rs) % qwg == 0) ? 1u : 0u;
-    uint32_t total;
-    const uint32_t pos = carry_n + block_scan<NT>(ts, sh, total) - ts;
-    if (ts && pos < (uint32_t)bound) tiles[pos] = make_int2(t, q);
-    carry_rs = max(carry_rs, smax[NT - 1]);
-    carry_n += total;
-    __syncthreads();
-  }
-  if (tid == 0) {
-    const bool fits = carry_n <= (uint32_t)bound;
-    *ntiles = fits ? carry_n : 0u;
-    *fallback = fits ? 0u : (uint32_t)T;
-  }
+  build_tile_table<NT>(q_seq, T, qwg, bound, tiles, ntiles, fallback, smax, sh);
 }
 
 hipError_t launch_prefill_tiles(const int32_t *q_seq, int T, int h, int bound, int2 *tiles, uint32_t *ntiles,

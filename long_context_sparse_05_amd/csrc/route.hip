@@ -21,6 +21,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "route_finish.hpp"
+#include "tiles.hpp"
 
 namespace misa {
 
@@ -189,11 +190,18 @@ __global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a) {
 }
 
 // One workgroup per query: the partial sums reduced in a fixed order,
-// weighted and ranked (route_finish.hpp).
+// weighted and ranked (route_finish.hpp).  With a tile table requested, one
+// more workgroup (the last) builds it for the grouped scoring that follows.
 __global__ __launch_bounds__(256) void route_final_kernel(RouteArgs a) {
   __shared__ float red[4][MISA_MAX_HEADS_DEV];
   __shared__ float gs[MISA_MAX_HEADS_DEV];
   const int t = blockIdx.x;
+  if (t == a.T) {  // uniform: the tile table
+    __shared__ int smax[256];
+    __shared__ uint32_t tsh[256 / kWave + 4];
+    build_tile_table<256>(a.q_seq, a.T, a.tqwg, a.tbound, a.tiles, a.tcount, a.tcount + 1, smax, tsh);
+    return;
+  }
   const int nparts = a.nchunks + 1;
   route_finish(a.partial + (size_t)t * nparts * a.H, nparts, a.H, a.w + (size_t)t * a.H, a.mode, a.h,
                red, gs, a.g ? a.g + (size_t)t * a.H : nullptr, a.heads + (size_t)t * a.h, nullptr);
@@ -481,7 +489,8 @@ hipError_t launch_route_partial(const RouteArgs &a, hipStream_t st) {
 hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
   hipError_t e = launch_route_partial(a, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(route_final_kernel, dim3(a.T), dim3(256), 0, st, a);
+  if (a.tiles && (!a.tcount || a.tqwg < 1 || a.tbound < 1)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(route_final_kernel, dim3(a.T + (a.tiles ? 1 : 0)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -39,11 +39,11 @@ constexpr int kKeyRowLds = 272;  // bytes per key row in the LDS tile (256 + 16)
 // 128 registers (two workgroups, sixteen waves, per CU: more key loads in
 // flight), and for direct rows of four tiles (64 heads: 200 registers, two
 // waves per SIMD, about 256 workgroups of 4096 keys -- 46.6 -> 46.0 us at
-// 32 x 32768 keys); four otherwise.  (RLIST launches keep four: eight would
-// spill there.)
+// 32 x 32768 keys); four otherwise.  (RLIST launches of four tiles keep
+// four: eight would spill there.)
 template <int HT, bool GATHER, bool RLIST = false>
 constexpr int score_waves() {
-  return !GATHER && !RLIST && (HT == 1 || HT == 4) ? 8 : 4;
+  return !GATHER && (HT == 1 || (HT == 4 && !RLIST)) ? 8 : 4;
 }
 
 // One (chunk, row) of the scoring: the body of score_rows_kernel.
