@@ -33,6 +33,9 @@ __device__ __forceinline__ uint4 load_nt16(const void *p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// An LDS address, for the buffer loads that write LDS directly.
+typedef __attribute__((address_space(3))) void lds_void;
+
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

@@ -85,6 +85,18 @@ __device__ __forceinline__ void score_row_chunk(const ScoreArgs &a, const int t)
   }
 
   const size_t seq_base = (size_t)a.q_seq[t] * a.Lmax;
+  // Direct rows request their first step's keys (those of load_step below)
+  // before the router prologue and the query loads, so that the stream is
+  // under way while the heads are ranked and loaded.
+  uint4 ka[U][4];
+  if constexpr (!GATHER) {
+    const int cw = c0 + wave * 16 * U + grp;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ka[u][i] = load_nt16(a.keys + (seq_base + (size_t)min(cw + u * 16 + 4 * i, c1 - 1)) * kD + col * 8);
+  }
   if constexpr (ROUTE) {  // the router's last step: reduce the partials, rank the heads
     route_finish(a.partial + (size_t)t * a.nparts * a.H, a.nparts, a.H, a.w + (size_t)t * a.H, a.mode,
                  a.nh, rred, rgs, (blockIdx.x == 0 && a.g_out) ? a.g_out + (size_t)t * a.H : nullptr,
@@ -175,7 +187,7 @@ __device__ __forceinline__ void score_row_chunk(const ScoreArgs &a, const int t)
   const int stride = NW * 16 * U;
   const int wstart = c0 + wave * 16 * U;
   const int nsteps = wstart < c1 ? (c1 - wstart + stride - 1) / stride : 0;
-  uint4 ka[U][4], kb2[U][4];
+  uint4 kb2[U][4];
 
   auto process_step = [&](int base, const uint4 (&kv)[U][4]) {
     float part[U];
@@ -220,7 +232,7 @@ __device__ __forceinline__ void score_row_chunk(const ScoreArgs &a, const int t)
   // steps leave the loop), so the compiler waits only for the step it
   // processes.
   if (nsteps > 0) {
-    load_step(wstart, ka);
+    if constexpr (GATHER) load_step(wstart, ka);
     for (int st = 0;; st += 2) {
       const int b0 = wstart + st * stride;
       if (st + 1 >= nsteps) {

@@ -731,7 +731,9 @@ def test_gpu_invariants(seed):
 
 
 # ------------------------------------------------------------ fused indexer
-@pytest.mark.parametrize("S,Lmax,T,H,seed", CASES[:4])
+# (H = 128: the fused scoring prologue reads the routed query rows from
+# memory instead of staging the row's heads in LDS)
+@pytest.mark.parametrize("S,Lmax,T,H,seed", CASES[:4] + [CASES[5]])
 @pytest.mark.parametrize("mode", [0, 1])
 def test_indexer_fused_equals_separate_calls(S, Lmax, T, H, seed, mode):
     """misa_indexer = misa_route then misa_score_topk, bit for bit; its
