@@ -25,6 +25,7 @@
 // Many rows, or short rows: one workgroup per row (topk_rowselect_kernel),
 // or for rows of 16K..128K columns first the streamed select of
 // topk_stream_kernel.
+#include <cmath>
 #include <type_traits>
 
 #include "common.hpp"
@@ -600,10 +601,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_flagged_kernel(TopkArgs a) {
 // cache lines a store); below, the block scan's layout costs less
 constexpr uint32_t kRunOutMin = 4096;
 
-template <bool MAP>
+// SPEC: entries per lane loaded ahead, per list (in the first round of
+// loads; the rest of a longer list follows in further rounds)
+template <bool MAP, int SPEC>
 __global__ __launch_bounds__(kSelThreads) void topk_merge_kernel(TopkArgs a) {
   constexpr int NT = kSelThreads, NW = NT / kWave;
-  constexpr int SPEC = 8;  // entries per lane loaded ahead, per list
   constexpr int PER = kSelCap / NT;
   constexpr int NB = kHistBins;  // bins over the union's key range
   __shared__ SelLds L;
@@ -831,10 +833,19 @@ __global__ __launch_bounds__(256) void topk_lists_kernel(TopkArgs a) {
 
 hipError_t launch_topk_merge(const TopkArgs &a, hipStream_t st) {
   if (a.nwg < 1 || a.nwg > kMaxLists) return hipErrorInvalidValue;
-  if (a.map)
-    hipLaunchKernelGGL(topk_merge_kernel<true>, dim3(a.rows), dim3(kSelThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(topk_merge_kernel<false>, dim3(a.rows), dim3(kSelThreads), 0, st, a);
+  // a list's expected length (its chunk's quota when the rows are whole):
+  // four entries a lane ahead cover it when it is at most 240 (k = 2048 over
+  // 32 lists: about 128), eight otherwise (k' = 8192: about 370)
+  const double e = (double)a.k / a.nwg;
+  const bool short_lists = e + 6.0 * std::sqrt(e) + 16.0 <= 240.0;
+  const dim3 grid(a.rows), block(kSelThreads);
+  if (a.map) {
+    if (short_lists) hipLaunchKernelGGL((topk_merge_kernel<true, 4>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((topk_merge_kernel<true, 8>), grid, block, 0, st, a);
+  } else {
+    if (short_lists) hipLaunchKernelGGL((topk_merge_kernel<false, 4>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((topk_merge_kernel<false, 8>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
