@@ -816,7 +816,7 @@ static HisaArgs make_hisa_args(const misa_batch *b, const float *pooled, int B, 
   a.nh = heads ? h : b->H;
   a.B = B;
   a.Mmax = (b->Lmax + B - 1) / B;
-  a.nchunks = (a.Mmax + kRouteChunk - 1) / kRouteChunk;
+  a.nchunks = (a.Mmax + kHisaChunk - 1) / kHisaChunk;
   return a;
 }
 

@@ -119,10 +119,10 @@ __global__ __launch_bounds__(256) void hisa_block_kernel(HisaArgs a) {
     return;
   }
 
-  const int b0 = ch * kRouteChunk;
+  const int b0 = ch * kHisaChunk;
   const int b = b0 + wave * 16 + col;
   if (b0 >= bt) {  // no complete block here: -inf past the query's own block
-    for (int bb = b0 + tid; bb < min(b0 + kRouteChunk, a.Mmax); bb += 256)
+    for (int bb = b0 + tid; bb < min(b0 + kHisaChunk, a.Mmax); bb += 256)
       if (bb > bt) srow[bb] = -INFINITY;
     return;
   }

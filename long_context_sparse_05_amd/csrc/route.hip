@@ -9,12 +9,12 @@
 // Blocks b < floor(p_t/B) are complete and come from the pooled cache; the
 // query's own last block is pooled here from the raw keys of [bB, p_t].
 //
-// route_partial_kernel: one workgroup per (query, 64 complete blocks); the
-// H x 64 affinities are an MFMA contraction over d = 128 with the query's
-// head rows as A and 16 pooled blocks per B tile.  The pooled keys are fp32;
-// each is split exactly into three bf16 terms (hi + mid + lo), so three
-// bf16 MFMAs give the fp32 dot product with exact products and fp32
-// accumulation.  The extra workgroup per query (index nchunks) pools the
+// route_partial_kernel: one workgroup per (query, kRouteChunk complete
+// blocks); the H x kRouteChunk affinities are an MFMA contraction over
+// d = 128 with the query's head rows as A and 16 pooled blocks per B tile.
+// The pooled keys are fp32; each is split exactly into three bf16 terms
+// (hi + mid + lo), so three bf16 MFMAs give the fp32 dot product with exact
+// products and fp32 accumulation.  The extra workgroup per query (index nchunks) pools the
 // tail block and does its dot products on the vector ALUs.
 // route_final_kernel: one wave per query sums the partials in a fixed order,
 // applies the weight and selects the top-h heads by (g desc, head id asc).
@@ -138,53 +138,71 @@ __global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) qa[ht][s] = as_bf16x8(mask_u4(*(const uint4 *)(qr + s * 32), mq));
   }
-  const int b = b0 + wave * 16 + col;
-  const bool ok = b < bt;
-  const uint32_t mb = ok ? 0xFFFFFFFFu : 0u;
-  const float *pb = a.pooled + ((size_t)sq * a.Mmax + (ok ? b : 0)) * kD + grp * 8;
-  uint4 xr[4][2];
+  // The wave's G groups of 16 blocks (group g: blocks b0 + (4g + wave)*16 ..
+  // + 15, one per lane column): all loads first, then per group the three
+  // MFMA planes, the ReLU and the sum over the group's blocks.
+  constexpr int G = kRouteChunk / 64;
+  static_assert(G * 64 == kRouteChunk, "whole groups of 16 blocks for each of the four waves");
+  uint4 xr[G][4][2];
+  bool okg[G];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    xr[s][0] = mask_u4(*(const uint4 *)(pb + s * 32), mb);
-    xr[s][1] = mask_u4(*(const uint4 *)(pb + s * 32 + 4), mb);
-  }
-  f32x4 acc[HT];
+  for (int g = 0; g < G; ++g) {
+    const int b = b0 + (g * 4 + wave) * 16 + col;
+    const bool ok = b < bt;
+    okg[g] = ok;
+    const uint32_t mb = ok ? 0xFFFFFFFFu : 0u;
+    const float *pb = a.pooled + ((size_t)sq * a.Mmax + (ok ? b : 0)) * kD + grp * 8;
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) acc[ht] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const uint4 x0 = xr[s][0], x1 = xr[s][1];
-    const float xs[8] = {__uint_as_float(x0.x), __uint_as_float(x0.y), __uint_as_float(x0.z),
-                         __uint_as_float(x0.w), __uint_as_float(x1.x), __uint_as_float(x1.y),
-                         __uint_as_float(x1.z), __uint_as_float(x1.w)};
-    u16x8 hi, mi, lo;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint16_t h16, m16, l16;
-      split3(xs[e], h16, m16, l16);
-      hi[e] = h16;
-      mi[e] = m16;
-      lo[e] = l16;
-    }
-    const bf16x8 bh = __builtin_bit_cast(bf16x8, hi);
-    const bf16x8 bm = __builtin_bit_cast(bf16x8, mi);
-    const bf16x8 bl = __builtin_bit_cast(bf16x8, lo);
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      acc[ht] = mfma16(qa[ht][s], bh, acc[ht]);
-      acc[ht] = mfma16(qa[ht][s], bm, acc[ht]);
-      acc[ht] = mfma16(qa[ht][s], bl, acc[ht]);
+    for (int s = 0; s < 4; ++s) {
+      xr[g][s][0] = mask_u4(*(const uint4 *)(pb + s * 32), mb);
+      xr[g][s][1] = mask_u4(*(const uint4 *)(pb + s * 32 + 4), mb);
     }
   }
-  // ReLU, then sum over this wave's 16 blocks (the 16 lanes of a group).
+  float rs[HT][4];
 #pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
+  for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float v = row_sum16(ok ? fmaxf(acc[ht][r], 0.f) : 0.f);
-      if (col == 0) part[wave][ht * 16 + grp * 4 + r] = v;
+    for (int r = 0; r < 4; ++r) rs[ht][r] = 0.f;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    f32x4 acc[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) acc[ht] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 x0 = xr[g][s][0], x1 = xr[g][s][1];
+      const float xs[8] = {__uint_as_float(x0.x), __uint_as_float(x0.y), __uint_as_float(x0.z),
+                           __uint_as_float(x0.w), __uint_as_float(x1.x), __uint_as_float(x1.y),
+                           __uint_as_float(x1.z), __uint_as_float(x1.w)};
+      u16x8 hi, mi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint16_t h16, m16, l16;
+        split3(xs[e], h16, m16, l16);
+        hi[e] = h16;
+        mi[e] = m16;
+        lo[e] = l16;
+      }
+      const bf16x8 bh = __builtin_bit_cast(bf16x8, hi);
+      const bf16x8 bm = __builtin_bit_cast(bf16x8, mi);
+      const bf16x8 bl = __builtin_bit_cast(bf16x8, lo);
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        acc[ht] = mfma16(qa[ht][s], bh, acc[ht]);
+        acc[ht] = mfma16(qa[ht][s], bm, acc[ht]);
+        acc[ht] = mfma16(qa[ht][s], bl, acc[ht]);
+      }
     }
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rs[ht][r] += row_sum16(okg[g] ? fmaxf(acc[ht][r], 0.f) : 0.f);
   }
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (col == 0) part[wave][ht * 16 + grp * 4 + r] = rs[ht][r];
   __syncthreads();
   for (int j = tid; j < a.H; j += 256) out[j] = ((part[0][j] + part[1][j]) + part[2][j]) + part[3][j];
 }
