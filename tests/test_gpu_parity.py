@@ -362,6 +362,34 @@ def test_two_stage_select_on_scored_rows(concentrated, k):
             parity.check_set(idx[t], oi, lambda i: osc[t, i], n, k, parity.row_sbar(osc[t], n))
 
 
+@pytest.mark.parametrize("heavy_chunk", [0, 3])
+def test_two_stage_merge_list_longer_than_first_load_round(heavy_chunk):
+    """A chunk list longer than the merge's first round of loads (four
+    entries a lane, 256 a list, when the expected list is short): 2 rows of
+    40960 columns, k = 512, ten lists of 4096 columns whose quota is 111.
+    Every score is 0 except 280 columns of one chunk and 30 of each other
+    chunk at 1.0: the heavy chunk keeps its 280 tied entries (at most
+    2 quota + 64 = 286), the others their 30, and the top-512 -- the 512
+    lowest columns scoring 1.0 -- is proven by the lists, so the merge
+    itself, with the tail of the long list loaded in a second round, writes
+    it (checked exactly against the oracle's fp32 top-k)."""
+    abi = _abi()
+    rows, ld, k, chunk = 2, 40960, 512, 4096
+    rng = np.random.default_rng(17 + heavy_chunk)
+    v = np.zeros((rows, ld), np.float32)
+    for r in range(rows):
+        for c in range(ld // chunk):
+            m = 280 if c == heavy_chunk else 30
+            v[r, c * chunk + rng.choice(chunk, m, replace=False)] = 1.0
+    row_len = np.full(rows, ld, np.int32)
+    idx, val = abi.topk(torch.from_numpy(v).cuda(), torch.from_numpy(row_len).cuda(), k)
+    idx, val = np_(idx), np_(val)
+    for r in range(rows):
+        parity.check_exact_topk(idx[r], val[r], v[r], ld, k, orc.topk_f32)
+        ones = np.flatnonzero(v[r] == 1.0)
+        assert np.array_equal(np.sort(idx[r]), ones[:k])
+
+
 # ------------------------------------------------------- pooled-cache append
 @pytest.mark.parametrize("B", [1, 16, 64, 128])
 def test_pool_append_matches_fresh_pool(B):
