@@ -12,7 +12,9 @@
 // per-query cost is then O(H_I M) with no pooling pass).
 //
 // One wave per block: each lane loads 16 bytes (8 bf16) of one of 4
-// consecutive keys per step, so a wave streams 1 KiB contiguous per load;
+// consecutive keys per step, so a wave streams 1 KiB contiguous per load
+// (non-temporal: the keys are read once here, and plain loads stream at
+// about half the rate on this part);
 // fp32 partial sums are combined across the 4 lane groups with two xor
 // shuffles and the 16 lanes of the first group store the 512-byte row.
 #include "common.hpp"
@@ -42,7 +44,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t *keys, const i
   for (; i + 12 < hi; i += 16) {  // four keys per lane in flight
     uint4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *(const uint4 *)(base + (size_t)(i + 4 * u) * kD);
+    for (int u = 0; u < 4; ++u) v[u] = load_nt16(base + (size_t)(i + 4 * u) * kD);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
@@ -54,7 +56,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t *keys, const i
     }
   }
   for (; i < hi; i += 4) {
-    const uint4 v = *(const uint4 *)(base + (size_t)i * kD);
+    const uint4 v = load_nt16(base + (size_t)i * kD);
     const uint32_t x[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
