@@ -16,8 +16,9 @@
 //     so that the list holds a little more than the chunk's expected share
 //     of the row's top-k (select.hpp, chunk_list);
 //  2. topk_merge_kernel, one 1024-thread workgroup per row, loads the
-//     union of the lists into LDS, takes its exact top-k (12-bit digit
-//     histogram, then 8-bit digit passes over the threshold digit's keys)
+//     union of the lists into LDS, takes its exact top-k (a 4096-bin
+//     histogram over the union's key range, then the keys of the crossing
+//     bin ranked among themselves)
 //     and checks that the k-th key's digit is no lower than every chunk's
 //     cutoff, which proves no dropped entry belongs in the top-k; if the
 //     check fails (a chunk holds far more than its share, heavy ties) the
